@@ -1,0 +1,205 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE layer forward library, libmoe.so.
+ *
+ * One MoE layer forward of a dots3-note-style (DeepSeek-V3 lineage) model:
+ * sigmoid router with bias-for-selection top-k, dispatch into expert-sorted
+ * order, SwiGLU experts as grouped GEMMs, an always-on shared expert, and a
+ * weighted combine.
+ *
+ * Sources (page title, then the section or figure):
+ *  [DD] "Xiaohongshu dots3 note Open Source Deep Dive: 280B MoE Multimodal
+ *       Model" -- §3.1 Expert Routing Mechanism (Dots3MoELayer.forward),
+ *       §3.3 single-layer figure, §8.2 Ascend adaptation figure (FUSED_MC2:
+ *       dispatch -> gmm1 -> swiglu -> gmm2 -> combine).
+ *  [AA] "dots3-note 架构深度解析：16B 激活参数的 280B MoE 如何实现高效推理" --
+ *       «核心架构参数一览» table and «稀疏激活Top-8 路由» section (256 routed + 1
+ *       shared experts, top-8, sigmoid scoring, noaux_tc, norm_topk_prob,
+ *       hidden 5120, moe_intermediate 1536, BF16/FP8).
+ *  [D1] "Transformers 中的 dots.llm1（Dots1）模型" -- «MoE 路由与专家相关字段»
+ *       table (n_routed_experts, num_experts_per_tok, n_shared_experts,
+ *       norm_topk_prob, routed_scaling_factor, moe_intermediate_size) and
+ *       «并行策略字段» (packed gate_up_proj, down_proj, grouped_gemm).
+ *
+ * Conventions for every entry point:
+ *  - All tensor arguments are DEVICE pointers owned by the caller, row-major,
+ *    16-byte aligned.  The library never allocates, frees, synchronises or
+ *    copies to the host; it holds no mutable global state.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *  - Arguments are validated on the host before anything is enqueued; on an
+ *    error nothing is enqueued and no output is touched.  Launch failures
+ *    return MOE_ERR_HIP.  Device faults surface at the caller's next sync.
+ *  - T == 0 is a valid no-op returning MOE_OK.
+ *  - Results are deterministic: no floating-point atomics anywhere.
+ *  - Calls on different streams are independent if they use different
+ *    outputs and workspaces.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* moe_stream_t; /* hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, misaligned pointer, bad size  */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but not supported by this library      */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required   */
+  MOE_ERR_HIP = -4          /* a HIP launch or API call failed              */
+} moe_status_t;
+
+typedef enum {
+  MOE_F32 = 0,      /* IEEE fp32                                             */
+  MOE_BF16 = 1,     /* bfloat16                                              */
+  MOE_FP8_E4M3 = 2  /* OCP FP8 E4M3 (bias 7, max 448, no inf), gfx950 native */
+} moe_dtype_t;
+
+/* Layer shape and options; field names follow the model config fields
+ * [AA «核心架构参数一览»; D1 «MoE 路由与专家相关字段»]. */
+typedef struct moe_config {
+  int32_t T;        /* tokens (batch * sequence, flattened)                 */
+  int32_t H;        /* hidden_size; multiple of 128                         */
+  int32_t E;        /* n_routed_experts; 1..512                             */
+  int32_t S;        /* n_shared_experts; 0..4                               */
+  int32_t k;        /* num_experts_per_tok; 1..min(E, 16)                   */
+  int32_t I;        /* moe_intermediate_size of a routed expert; mult. of 128 */
+  int32_t I_shared; /* intermediate size of a shared expert; must equal I   */
+  int32_t norm_topk_prob;      /* 1: renormalise the k chosen scores        */
+  float routed_scaling_factor; /* multiplies the routing weights            */
+  int32_t act_dtype;    /* x, router weight and output: MOE_F32 | MOE_BF16  */
+  int32_t expert_dtype; /* expert weights: MOE_F32 (act F32), MOE_BF16 or
+                           MOE_FP8_E4M3 (act BF16)                          */
+} moe_config_t;
+
+/* Weights of one layer (device pointers).
+ *  w_router     [E, H]        act_dtype; the gate Linear(H -> E, no bias)
+ *                             [DD §3.1; §3.3 "Gate (Linear 5120→256)"]
+ *  router_bias  [E]           fp32; added to the sigmoid scores for the
+ *                             choice of experts only (noaux_tc [AA])
+ *  w_gate_up    [E, 2I, H]    expert_dtype; rows [0, I) gate, [I, 2I) up
+ *                             (packed gate_up_proj [D1 «并行策略字段»])
+ *  w_down       [E, H, I]     expert_dtype (down_proj)
+ *  w_sh_gate_up [S, 2I, H], w_sh_down [S, H, I]: the shared experts.
+ *  s_*          fp32 block scales, FP8 only (NULL otherwise): one scale per
+ *               128 x 128 block of the matching weight, i.e. s_gate_up
+ *               [E, 2I/128, H/128], s_down [E, H/128, I/128], and the same
+ *               with S for the shared ones.  Dequantised weight =
+ *               e4m3 code * block scale.                                   */
+typedef struct moe_weights {
+  const void* w_router;
+  const float* router_bias;
+  const void* w_gate_up;
+  const void* w_down;
+  const float* s_gate_up;
+  const float* s_down;
+  const void* w_sh_gate_up;
+  const void* w_sh_down;
+  const float* s_sh_gate_up;
+  const float* s_sh_down;
+} moe_weights_t;
+
+/* Human-readable text of a status code (static storage). */
+const char* moe_status_string(moe_status_t status);
+
+/* Library version string, e.g. "moe-gfx950 1.0". */
+const char* moe_version(void);
+
+/* Bytes of workspace that moe_layer_forward needs for this config (0 if the
+ * config is invalid).  moe_route, moe_dispatch, moe_grouped_ffn and
+ * moe_combine accept the same workspace; each needs at most this much. */
+size_t moe_workspace_size(const moe_config_t* cfg);
+
+/* Router [DD §3.1 steps 1-2; AA «稀疏激活»]: for every token t
+ *   l[t,e] = Σ_h x[t,h] * w_router[e,h]      (fp32 accumulate, never bf16)
+ *   s = 1 / (1 + exp(-l));   c = s + router_bias   (c used for the choice only)
+ *   topk_idx[t, 0..k) = the k experts of largest c, in decreasing c, the lower
+ *                       expert index first among equal c
+ *   topk_w[t, j] = s[t, idx_j] / Σ_j' s[t, idx_j'] * routed_scaling_factor
+ *                  (without the division when norm_topk_prob == 0)
+ * x [T, H] act_dtype; topk_idx [T, k] int32; topk_w [T, k] fp32.
+ * tie_counts: NULL, or int32[2] that receives the number of tokens whose
+ * k-th and (k+1)-th keys (index 0), resp. some two consecutive chosen keys
+ * (index 1), differ by <= 1e-6 in fp32 -- tokens where another choice or slot
+ * order is equally valid at fp32 precision.  Workspace: holds the fp32
+ * logits [T, E]. */
+moe_status_t moe_route(const moe_config_t* cfg, const void* x, const moe_weights_t* w,
+                       int32_t* topk_idx, float* topk_w, int32_t* tie_counts,
+                       void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* Dispatch [DD §3.1 per-expert mask gather; §8.2 "dispatch"]: group the T*k
+ * (token, slot) pairs f = t*k + j by expert e = topk_idx[t, j]:
+ *   counts[e]   = #{f : e(f) = e}                         int32 [E]
+ *   offsets[e]  = Σ_{e' < e} counts[e'], offsets[E] = T*k  int32 [E+1]
+ *   inv[f]      = offsets[e(f)] + #{f' < f : e(f') = e(f)} int32 [T*k]
+ *   perm[inv[f]] = f                                       int32 [T*k]
+ * i.e. a stable counting sort, bit-exact and deterministic.  topk_idx values
+ * must lie in [0, E) (not checked on the device).  Workspace: small. */
+moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* inv, void* workspace,
+                          size_t workspace_bytes, moe_stream_t stream);
+
+/* Expert FFNs as grouped GEMMs [D1 «并行策略字段» grouped_gemm; DD §8.2
+ * "gmm1 -> swiglu -> gmm2"].  For sorted row p of expert e (offsets[e] <= p <
+ * offsets[e+1]) and its token t = perm[p] / k:
+ *   h = SiLU(Wg_e x_t) * (Wu_e x_t),  SiLU(z) = z / (1 + exp(-z))
+ *   y_sorted[p] = Wd_e h                                  act_dtype [T*k, H]
+ * and for every shared expert s and token t:
+ *   y_shared[s, t] = Wd_s (SiLU(Wg_s x_t) * (Wu_s x_t))   act_dtype [S, T, H]
+ * fp32 accumulation; h is rounded to the activation type (bf16) between the
+ * two GEMMs.  FP8: x and h are quantised per token per 128 channels to e4m3
+ * with scale amax/448 (fp32) before their GEMM; weights use their block
+ * scales.  perm and offsets are moe_dispatch outputs (device).  Workspace:
+ * h and the tile schedule. */
+moe_status_t moe_grouped_ffn(const moe_config_t* cfg, const void* x, const moe_weights_t* w,
+                             const int32_t* perm, const int32_t* offsets, void* y_sorted,
+                             void* y_shared, void* workspace, size_t workspace_bytes,
+                             moe_stream_t stream);
+
+/* The two halves of moe_grouped_ffn, for callers that time or overlap them:
+ * gate/up + SwiGLU writes h (returned through the workspace), down reads it.
+ * moe_expert_gate_up must run before moe_expert_down on the same workspace. */
+moe_status_t moe_expert_gate_up(const moe_config_t* cfg, const void* x, const moe_weights_t* w,
+                                const int32_t* perm, const int32_t* offsets, void* workspace,
+                                size_t workspace_bytes, moe_stream_t stream);
+moe_status_t moe_expert_down(const moe_config_t* cfg, const moe_weights_t* w, void* y_sorted,
+                             void* y_shared, void* workspace, size_t workspace_bytes,
+                             moe_stream_t stream);
+
+/* Combine [DD §3.1 weighted add; §3.3 "Weighted sum" then shared "add"]:
+ *   out[t] = Σ_s y_shared[s, t] + Σ_{j=0}^{k-1} topk_w[t, j] * y_sorted[inv[t*k + j]]
+ * accumulated in fp32 in exactly this order (s ascending, then j ascending),
+ * one rounding to act_dtype.  No atomics.  out [T, H] act_dtype. */
+moe_status_t moe_combine(const moe_config_t* cfg, const void* y_sorted, const void* y_shared,
+                         const float* topk_w, const int32_t* inv, void* out, moe_stream_t stream);
+
+/* FP8 activation quantisation, the input step of the FP8 expert GEMMs
+ * (FP8 precision [AA «核心架构参数一览»]; per-token-per-128-channel scales):
+ * for row r and channel c of x [rows, cols] bf16,
+ *   scale[r, c/128] = amax over the 128-channel block / 448  (fp32; 1.0 for
+ *                     an all-zero block), divided in correctly rounded fp32
+ *   q[r, c] = e4m3(x[r, c] / scale[r, c/128]), round to nearest even
+ * q [rows, cols] uint8 e4m3 codes; scales [rows, cols/128] fp32.
+ * cols must be a multiple of 128; x and q 16-byte aligned. */
+moe_status_t moe_quantize_fp8(const void* x_bf16, int32_t rows, int32_t cols, uint8_t* q,
+                              float* scales, moe_stream_t stream);
+
+/* The whole layer [DD §3.1 Dots3MoELayer.forward]: route -> dispatch ->
+ * grouped gate/up + SwiGLU -> grouped down -> combine, enqueued back to back
+ * with no host synchronisation.  out [T, H] act_dtype.
+ * opt_counts: NULL or int32[E], receives the per-expert row counts.
+ * opt_tie_counts: NULL or int32[2], see moe_route.
+ * workspace: at least moe_workspace_size(cfg) bytes, 256-byte aligned. */
+moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                               void* out, int32_t* opt_counts, int32_t* opt_tie_counts,
+                               void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,28 @@
+"""MI355X (gfx950) MoE layer forward: sigmoid/noaux_tc router, stable
+dispatch, grouped SwiGLU expert GEMMs (bf16 / fp8 e4m3 MFMA), shared expert
+and deterministic combine, as hand-written HIP kernels behind the C ABI of
+include/moe.h (libmoe.so).
+
+This package is the ctypes binding (``_lib``) plus device-buffer plumbing
+(``device``).  The binding loads on first use of any of its names and raises
+ImportError if libmoe.so has not been built; there is no other code path.
+``python -m sparse_moe_expert_amd.build`` builds the library.
+"""
+import importlib
+
+_BINDING = (
+    "DTYPES", "EXPORTS", "LIB", "LIB_PATH", "MOE_BF16", "MOE_ERR_HIP", "MOE_ERR_INVALID_ARG",
+    "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_F32", "MOE_FP8_E4M3", "MOE_OK", "MoEError",
+    "make_config", "make_weights", "moe_combine", "moe_config_t", "moe_dispatch",
+    "moe_expert_down", "moe_expert_gate_up", "moe_grouped_ffn", "moe_layer_forward",
+    "moe_quantize_fp8", "moe_route", "moe_weights_t", "moe_workspace_size", "status_string",
+    "version",
+)
+
+__all__ = list(_BINDING)
+
+
+def __getattr__(name):
+    if name in _BINDING:
+        return getattr(importlib.import_module("._lib", __name__), name)
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")

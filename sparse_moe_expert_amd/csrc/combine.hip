@@ -1,0 +1,148 @@
+// Combine and FP8 activation quantisation (gfx950).
+//
+// Combine: out[t] = Σ_s y_shared[s, t] + Σ_j w[t, j] * y_sorted[inv[t*k + j]],
+// the weighted sum of the k expert outputs plus the always-on shared expert
+// (Deep Dive §3.1 forward; §3.3 figure "Weighted sum" then "Shared Expert
+// (always) … add").  One workgroup per token gathers its k rows in slot order;
+// fp32 accumulation in a fixed order, one rounding at the store, no atomics.
+//
+// Quantisation: per row and 128 channels, scale = amax / 448 (fp32, 1 for an
+// all-zero block) and code = e4m3(v / scale), round to nearest even -- the
+// FP8 format of "dots3-note 架构深度解析" (mlqm.cn, «核心架构参数一览»:
+// BF16、FP8) at per-token-per-128-channel granularity.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+template <int AK>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
+                                                      const void* __restrict__ ysh,
+                                                      const float* __restrict__ w,
+                                                      const int32_t* __restrict__ inv,
+                                                      void* __restrict__ out, int T, int H, int k,
+                                                      int S) {
+  constexpr int VEC = (AK == K_BF16) ? 8 : 4;
+  __shared__ float ws[kMaxTopK];
+  __shared__ long long rs[kMaxTopK];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) {
+    ws[threadIdx.x] = w[static_cast<long long>(t) * k + threadIdx.x];
+    rs[threadIdx.x] = inv[static_cast<long long>(t) * k + threadIdx.x];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x * VEC; c < H; c += blockDim.x * VEC) {
+    float acc[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+    if constexpr (AK == K_BF16) {
+      const uint16_t* ysh16 = static_cast<const uint16_t*>(ysh);
+      const uint16_t* y16 = static_cast<const uint16_t*>(y);
+      for (int s = 0; s < S; ++s) {
+        const uint4 v = *reinterpret_cast<const uint4*>(
+            ysh16 + (static_cast<long long>(s) * T + t) * H + c);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += bf16_to_f32(static_cast<uint16_t>(u[i]));
+          acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(u[i] >> 16));
+        }
+      }
+      for (int j = 0; j < k; ++j) {
+        const float wj = ws[j];
+        const uint4 v = *reinterpret_cast<const uint4*>(y16 + rs[j] * H + c);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(u[i])), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(u[i] >> 16)), acc[2 * i + 1]);
+        }
+      }
+      uint4 o;
+      o.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
+      o.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
+      o.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
+      o.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + static_cast<long long>(t) * H + c) = o;
+    } else {
+      const float* yshf = static_cast<const float*>(ysh);
+      const float* yf = static_cast<const float*>(y);
+      for (int s = 0; s < S; ++s) {
+        const float4 v = *reinterpret_cast<const float4*>(yshf + (static_cast<long long>(s) * T + t) * H + c);
+        acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
+      }
+      for (int j = 0; j < k; ++j) {
+        const float wj = ws[j];
+        const float4 v = *reinterpret_cast<const float4*>(yf + rs[j] * H + c);
+        acc[0] = fmaf(wj, v.x, acc[0]);
+        acc[1] = fmaf(wj, v.y, acc[1]);
+        acc[2] = fmaf(wj, v.z, acc[2]);
+        acc[3] = fmaf(wj, v.w, acc[3]);
+      }
+      *reinterpret_cast<float4*>(static_cast<float*>(out) + static_cast<long long>(t) * H + c) =
+          float4{acc[0], acc[1], acc[2], acc[3]};
+    }
+  }
+}
+
+// 16 lanes per 128-channel block, 8 channels per lane.
+__global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t* __restrict__ x,
+                                                             int rows, int cols,
+                                                             uint8_t* __restrict__ q,
+                                                             float* __restrict__ scales) {
+  const long long gid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int nblk = cols / kQBlock;
+  const long long blk = gid >> 4;
+  const int sub = static_cast<int>(gid & 15);
+  const bool on = blk < static_cast<long long>(rows) * nblk;
+  float v[8];
+  float amax = 0.f;
+  const long long base = on ? (blk / nblk) * cols + (blk % nblk) * kQBlock + sub * 8 : 0;
+  if (on) {
+    const uint4 u = *reinterpret_cast<const uint4*>(x + base);
+    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32(static_cast<uint16_t>(w4[i]));
+      v[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w4[i] >> 16));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  if (!on) return;
+  const float scale = (amax == 0.f) ? 1.0f : amax / 448.0f;
+  uint2 codes;
+  codes.x = f32x4_to_e4m3(v[0] / scale, v[1] / scale, v[2] / scale, v[3] / scale);
+  codes.y = f32x4_to_e4m3(v[4] / scale, v[5] / scale, v[6] / scale, v[7] / scale);
+  *reinterpret_cast<uint2*>(q + base) = codes;
+  if (sub == 0) scales[blk] = scale;
+}
+
+}  // namespace
+
+hipError_t launch_combine(int act_kind, const void* y, const void* ysh, const float* w,
+                          const int32_t* inv, void* out, int T, int H, int k, int S,
+                          hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (act_kind == K_BF16)
+    hipLaunchKernelGGL(combine_kernel<K_BF16>, dim3(T), dim3(256), 0, st, y, ysh, w, inv, out, T,
+                       H, k, S);
+  else
+    hipLaunchKernelGGL(combine_kernel<K_F32>, dim3(T), dim3(256), 0, st, y, ysh, w, inv, out, T,
+                       H, k, S);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_fp8(const uint16_t* x_bf16, int rows, int cols, uint8_t* q,
+                                 float* scales, hipStream_t st) {
+  const long long threads = static_cast<long long>(rows) * (cols / kQBlock) * 16;
+  if (threads <= 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)),
+                     dim3(256), 0, st, x_bf16, rows, cols, q, scales);
+  return hipGetLastError();
+}
+
+}  // namespace moe

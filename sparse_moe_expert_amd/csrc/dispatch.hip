@@ -1,0 +1,213 @@
+// Dispatch: per-expert histogram, exclusive scan and stable permutation of the
+// T*k (token, slot) pairs into expert-sorted order (gfx950), plus the device
+// tile schedule of the grouped GEMMs.
+//
+// The order inside an expert is ascending flat index f = t*k + j -- the order
+// in which the per-expert mask gathers tokens (x[mask]) in the Dots3MoELayer
+// loop of the Deep Dive §3.1 -- so the result is a stable counting sort, the
+// "dispatch" step of the §8.2 figure.  Integer only, no float, deterministic:
+//   1. hist:    one wave per 1024-pair chunk counts its pairs per expert
+//               (LDS atomics on integers; order-independent).
+//   2. scan:    per expert, exclusive scan over chunks; then over experts.
+//   3. scatter: one wave per chunk walks its pairs 64 at a time; lanes with
+//               the same expert find each other with 9 ballots (bits of the
+//               expert id), take rank = earlier peers, and the lowest peer
+//               advances the expert's running position.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kExpertBits = 9;  // kMaxExperts = 512
+static_assert((1 << kExpertBits) == kMaxExperts, "expert id bits");
+
+__global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __restrict__ idx,
+                                                            int n, int E, int nchunks,
+                                                            int32_t* __restrict__ chunk_counts) {
+  __shared__ int32_t hist[kWavesPerBlock][kMaxExperts];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kWavesPerBlock * kMaxExperts; i += blockDim.x)
+    (&hist[0][0])[i] = 0;
+  __syncthreads();
+  const int c = blockIdx.x * kWavesPerBlock + wave;
+  if (c < nchunks) {
+    const int f0 = c * kDispatchChunk;
+    for (int r = 0; r < kDispatchChunk / 64; ++r) {
+      const int f = f0 + r * 64 + lane;
+      if (f < n) atomicAdd(&hist[wave][idx[f]], 1);
+    }
+  }
+  __syncthreads();
+  if (c < nchunks)
+    for (int e = lane; e < E; e += 64) chunk_counts[static_cast<long long>(c) * E + e] = hist[wave][e];
+}
+
+// Single block of 1024 threads.  Block-wide exclusive scan helper.
+__device__ int block_exclusive_scan(int v, int* sh, int* total) {
+  const int t = threadIdx.x;
+  sh[t] = v;
+  __syncthreads();
+  for (int off = 1; off < static_cast<int>(blockDim.x); off <<= 1) {
+    const int add = (t >= off) ? sh[t - off] : 0;
+    __syncthreads();
+    sh[t] += add;
+    __syncthreads();
+  }
+  const int incl = sh[t];
+  if (total) *total = sh[blockDim.x - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ chunk_counts,
+                                                             int nchunks, int E,
+                                                             int32_t* __restrict__ chunk_base,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets) {
+  __shared__ int sh[1024];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      const long long i = static_cast<long long>(c) * E + e;
+      const int v = chunk_counts[i];
+      chunk_base[i] = run;
+      run += v;
+    }
+  }
+  int total = 0;
+  const int excl = block_exclusive_scan(e < E ? run : 0, sh, &total);
+  if (e < E) {
+    counts[e] = run;
+    offsets[e] = excl;
+    for (int c = 0; c < nchunks; ++c) chunk_base[static_cast<long long>(c) * E + e] += excl;
+  }
+  if (e == 0) offsets[E] = total;
+}
+
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __restrict__ idx,
+                                                               int n, int E, int nchunks,
+                                                               const int32_t* __restrict__ chunk_base,
+                                                               int32_t* __restrict__ perm,
+                                                               int32_t* __restrict__ inv) {
+  __shared__ int32_t run[kWavesPerBlock][kMaxExperts];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = blockIdx.x * kWavesPerBlock + wave;
+  if (c < nchunks)
+    for (int e = lane; e < E; e += 64) run[wave][e] = chunk_base[static_cast<long long>(c) * E + e];
+  __syncthreads();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int r = 0; r < kDispatchChunk / 64; ++r) {
+    const int f = c * kDispatchChunk + r * 64 + lane;
+    const bool valid = (c < nchunks) && (f < n);
+    const int e = valid ? idx[f] : 0;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < kExpertBits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & below);
+    const int base = valid ? run[wave][e] : 0;
+    __syncthreads();  // every lane has read its base before any update
+    if (valid) {
+      const int pos = base + rank;
+      perm[pos] = f;
+      inv[f] = pos;
+      if (rank == 0) run[wave][e] = base + __popcll(peers);
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(1024) void build_groups_kernel(
+    const int32_t* __restrict__ offsets, int T, int k, int E, int S, GroupDesc* __restrict__ groups,
+    int32_t* __restrict__ totals, int bm_gu, int bm_dn, const char* w_gu, const float* s_gu,
+    const char* w_dn, const float* s_dn, const char* w_sh_gu, const float* s_sh_gu,
+    const char* w_sh_dn, const float* s_sh_dn, int H, int I, int esz, int fp8) {
+  __shared__ int sh[1024];
+  const int g = threadIdx.x;
+  const int G = E + S;
+  const int R = T * k;
+  int begin = 0, rows = 0;
+  if (g < E) {
+    begin = offsets[g];
+    rows = offsets[g + 1] - begin;
+  } else if (g < G) {
+    begin = R + (g - E) * T;
+    rows = T;
+  }
+  const int tg = (rows + bm_gu - 1) / bm_gu;
+  const int td = (rows + bm_dn - 1) / bm_dn;
+  int tot_g = 0, tot_d = 0;
+  const int ex_g = block_exclusive_scan(tg, sh, &tot_g);
+  const int ex_d = block_exclusive_scan(td, sh, &tot_d);
+  if (g < G) {
+    const bool shared = g >= E;
+    const long long e = shared ? g - E : g;
+    const long long gu_elems = 2ll * I * H, dn_elems = static_cast<long long>(H) * I;
+    const long long gu_sc = fp8 ? (2ll * I / kQBlock) * (H / kQBlock) : 0;
+    const long long dn_sc = fp8 ? (static_cast<long long>(H) / kQBlock) * (I / kQBlock) : 0;
+    GroupDesc d;
+    d.row_begin = begin;
+    d.rows = rows;
+    d.tile_begin_gu = ex_g;
+    d.tile_begin_dn = ex_d;
+    d.w_gu = (shared ? w_sh_gu : w_gu) + e * gu_elems * esz;
+    d.w_dn = (shared ? w_sh_dn : w_dn) + e * dn_elems * esz;
+    d.s_gu = fp8 ? (shared ? s_sh_gu : s_gu) + e * gu_sc : nullptr;
+    d.s_dn = fp8 ? (shared ? s_sh_dn : s_dn) + e * dn_sc : nullptr;
+    groups[g] = d;
+  }
+  if (g == 0) {
+    totals[0] = tot_g;
+    totals[1] = tot_d;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_groups_only(const int32_t* offsets, int T, int k, int E, int S,
+                              GroupDesc* groups, int32_t* totals, TileShape gu, TileShape dn,
+                              const void* w_gu, const float* s_gu, const void* w_dn,
+                              const float* s_dn, const void* w_sh_gu, const float* s_sh_gu,
+                              const void* w_sh_dn, const float* s_sh_dn, int H, int I,
+                              int expert_kind, hipStream_t st) {
+  hipLaunchKernelGGL(build_groups_kernel, dim3(1), dim3(1024), 0, st, offsets, T, k, E, S, groups,
+                     totals, gu.bm, dn.bm, static_cast<const char*>(w_gu), s_gu,
+                     static_cast<const char*>(w_dn), s_dn, static_cast<const char*>(w_sh_gu),
+                     s_sh_gu, static_cast<const char*>(w_sh_dn), s_sh_dn, H, I,
+                     static_cast<int>(kind_size(expert_kind)), expert_kind == K_FP8 ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const int32_t* topk_idx, int T, int k, int E, int S,
+                           int32_t* chunk_counts, int32_t* chunk_base, int nchunks,
+                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                           GroupDesc* groups, int32_t* totals, TileShape gu, TileShape dn,
+                           const void* w_gu, const float* s_gu, const void* w_dn,
+                           const float* s_dn, const void* w_sh_gu, const float* s_sh_gu,
+                           const void* w_sh_dn, const float* s_sh_dn, int H, int I,
+                           int expert_kind, hipStream_t st) {
+  const int n = T * k;
+  const int blocks = (nchunks + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL(dispatch_hist_kernel, dim3(blocks), dim3(256), 0, st, topk_idx, n, E,
+                     nchunks, chunk_counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, chunk_counts, nchunks, E,
+                     chunk_base, counts, offsets);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(blocks), dim3(256), 0, st, topk_idx, n, E,
+                     nchunks, chunk_base, perm, inv);
+  err = hipGetLastError();
+  if (err != hipSuccess || groups == nullptr) return err;
+  return launch_groups_only(offsets, T, k, E, S, groups, totals, gu, dn, w_gu, s_gu, w_dn, s_dn,
+                            w_sh_gu, s_sh_gu, w_sh_dn, s_sh_dn, H, I, expert_kind, st);
+}
+
+}  // namespace moe

@@ -1,0 +1,392 @@
+// Host entry points of libmoe: argument validation, workspace layout and the
+// launch sequence of one MoE layer forward (Deep Dive §3.1 Dots3MoELayer
+// forward; §8.2 figure: dispatch -> gmm1 -> swiglu -> gmm2 -> combine).
+//
+// Every check runs before the first launch, so an invalid call enqueues
+// nothing.  Nothing here allocates, frees, synchronises or copies to the
+// host; all state lives in the caller's buffers.
+#include <algorithm>
+#include <climits>
+#include <cmath>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+moe_status_t check_config(const moe_config_t* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->H <= 0 || c->E <= 0 || c->S < 0 || c->k <= 0 || c->I <= 0 ||
+      c->I_shared <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->k > c->E) return MOE_ERR_INVALID_ARG;
+  if (c->norm_topk_prob != 0 && c->norm_topk_prob != 1) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(c->routed_scaling_factor)) return MOE_ERR_INVALID_ARG;
+  if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->expert_dtype != MOE_F32 && c->expert_dtype != MOE_BF16 &&
+      c->expert_dtype != MOE_FP8_E4M3)
+    return MOE_ERR_INVALID_ARG;
+  if (c->E > kMaxExperts || c->S > kMaxShared || c->k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (c->H % kQBlock != 0 || c->I % kQBlock != 0) return MOE_ERR_UNSUPPORTED;
+  if (c->I_shared != c->I) return MOE_ERR_UNSUPPORTED;
+  // expert storage must match the activation type (FP8 experts take bf16 x)
+  if (c->act_dtype == MOE_F32 && c->expert_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (c->act_dtype == MOE_BF16 && c->expert_dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
+  // index arithmetic stays in int32 for rows and in int64 for element offsets
+  const long long R = static_cast<long long>(c->T) * c->k;
+  const long long rows_all = R + static_cast<long long>(c->S) * c->T;
+  if (rows_all > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int act_kind(const moe_config_t& c) { return c.act_dtype == MOE_F32 ? K_F32 : K_BF16; }
+int expert_kind(const moe_config_t& c) {
+  return c.expert_dtype == MOE_F32 ? K_F32 : c.expert_dtype == MOE_BF16 ? K_BF16 : K_FP8;
+}
+bool is_fp8(const moe_config_t& c) { return c.expert_dtype == MOE_FP8_E4M3; }
+
+moe_status_t check_weights(const moe_config_t& c, const moe_weights_t* w, bool router,
+                           bool experts) {
+  if (!w) return MOE_ERR_INVALID_ARG;
+  if (router) {
+    if (!w->w_router || !w->router_bias || !aligned16(w->w_router)) return MOE_ERR_INVALID_ARG;
+  }
+  if (experts) {
+    if (!w->w_gate_up || !w->w_down || !aligned16(w->w_gate_up) || !aligned16(w->w_down))
+      return MOE_ERR_INVALID_ARG;
+    if (c.S > 0 && (!w->w_sh_gate_up || !w->w_sh_down || !aligned16(w->w_sh_gate_up) ||
+                    !aligned16(w->w_sh_down)))
+      return MOE_ERR_INVALID_ARG;
+    if (is_fp8(c)) {
+      if (!w->s_gate_up || !w->s_down) return MOE_ERR_INVALID_ARG;
+      if (c.S > 0 && (!w->s_sh_gate_up || !w->s_sh_down)) return MOE_ERR_INVALID_ARG;
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status_t check_ws(const moe_config_t& c, void* ws, size_t bytes) {
+  const Layout L = make_layout(c);
+  if (L.total == 0) return MOE_OK;
+  if (!ws) return MOE_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return MOE_ERR_WORKSPACE;
+  if (bytes < L.total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+long long mtiles_upper(const moe_config_t& c, int bm) {
+  const long long R = static_cast<long long>(c.T) * c.k;
+  return R / bm + std::min<long long>(c.E, R) + 1 + static_cast<long long>(c.S) * ((c.T + bm - 1) / bm);
+}
+
+// ---------------------------------------------------------------- stages
+hipError_t run_route(const moe_config_t& c, const Layout& L, const void* x, const moe_weights_t& w,
+                     int32_t* idx, float* tw, int32_t* ties, void* ws, hipStream_t st) {
+  float* logits = at<float>(ws, L.logits);
+  GemmLaunch g{};
+  g.single_group_rows = c.T;
+  g.b_single = w.w_router;
+  g.N = c.E;
+  g.K = c.H;
+  g.A = x;
+  g.lda = c.H;
+  g.C = logits;
+  g.C2 = logits;
+  g.c_split = LLONG_MAX;
+  g.ldc = c.E;
+  hipError_t e = launch_gemm(act_kind(c), K_F32, L.router, g, st);
+  if (e != hipSuccess) return e;
+  if (ties) {
+    e = launch_zero_i32(ties, 2, st);
+    if (e != hipSuccess) return e;
+  }
+  return launch_router_topk(logits, w.router_bias, c.T, c.E, c.k, c.norm_topk_prob,
+                            c.routed_scaling_factor, idx, tw, ties, st);
+}
+
+hipError_t run_groups(const moe_config_t& c, const Layout& L, const int32_t* offsets,
+                      const moe_weights_t& w, void* ws, hipStream_t st) {
+  return launch_groups_only(offsets, c.T, c.k, c.E, c.S, at<GroupDesc>(ws, L.groups),
+                            at<int32_t>(ws, L.totals), L.gu, L.dn, w.w_gate_up, w.s_gate_up,
+                            w.w_down, w.s_down, w.w_sh_gate_up, w.s_sh_gate_up, w.w_sh_down,
+                            w.s_sh_down, c.H, c.I, expert_kind(c), st);
+}
+
+hipError_t run_gate_up(const moe_config_t& c, const Layout& L, const void* x, const int32_t* perm,
+                       void* ws, hipStream_t st) {
+  const bool fp8 = is_fp8(c);
+  if (fp8) {
+    hipError_t e = launch_quant_rows_fp8(static_cast<const uint16_t*>(x), c.T, c.H,
+                                         at<uint8_t>(ws, L.xq), at<float>(ws, L.xs), st);
+    if (e != hipSuccess) return e;
+  }
+  GemmLaunch g{};
+  g.groups = at<GroupDesc>(ws, L.groups);
+  g.num_groups = c.E + c.S;
+  g.total_mtiles = at<int32_t>(ws, L.totals);
+  g.dual = 1;
+  g.grid_mtiles_upper = static_cast<int>(mtiles_upper(c, L.gu.bm));
+  g.N = c.I;
+  g.K = c.H;
+  g.A = fp8 ? static_cast<const void*>(at<uint8_t>(ws, L.xq)) : x;
+  g.lda = c.H;
+  g.a_scale = fp8 ? at<float>(ws, L.xs) : nullptr;
+  g.perm = perm;
+  g.R = c.T * c.k;
+  g.k = c.k;
+  g.T = c.T;
+  g.C = at<char>(ws, L.h);
+  g.C2 = g.C;
+  g.c_split = LLONG_MAX;
+  g.ldc = c.I;
+  g.c_scale = fp8 ? at<float>(ws, L.hs) : nullptr;
+  return launch_gemm(expert_kind(c), fp8 ? K_FP8 : act_kind(c), L.gu, g, st);
+}
+
+hipError_t run_down(const moe_config_t& c, const Layout& L, void* y_sorted, void* y_shared,
+                    void* ws, hipStream_t st) {
+  const bool fp8 = is_fp8(c);
+  GemmLaunch g{};
+  g.groups = at<GroupDesc>(ws, L.groups);
+  g.num_groups = c.E + c.S;
+  g.total_mtiles = at<int32_t>(ws, L.totals) + 1;
+  g.dual = 0;
+  g.grid_mtiles_upper = static_cast<int>(mtiles_upper(c, L.dn.bm));
+  g.N = c.H;
+  g.K = c.I;
+  g.A = at<char>(ws, L.h);
+  g.lda = c.I;
+  g.a_scale = fp8 ? at<float>(ws, L.hs) : nullptr;
+  g.perm = nullptr;
+  g.R = c.T * c.k;
+  g.k = c.k;
+  g.T = c.T;
+  g.C = y_sorted;
+  g.C2 = y_shared;
+  g.c_split = static_cast<long long>(c.T) * c.k;
+  g.ldc = c.H;
+  return launch_gemm(expert_kind(c), act_kind(c), L.dn, g, st);
+}
+
+}  // namespace
+
+Layout make_layout(const moe_config_t& c) {
+  Layout L{};
+  const size_t T = static_cast<size_t>(c.T), H = c.H, E = c.E, S = c.S, k = c.k, I = c.I;
+  const size_t R = T * k, rows_all = R + S * T;
+  const size_t asz = c.act_dtype == MOE_F32 ? 4 : 2;
+  const bool fp8 = c.expert_dtype == MOE_FP8_E4M3;
+  L.nchunks = static_cast<int>((R + kDispatchChunk - 1) / kDispatchChunk);
+
+  // Tile shapes from the mean rows per routed expert (no device sync needed).
+  const double avg = E ? static_cast<double>(R) / static_cast<double>(E) : 0.0;
+  const int bm = avg <= 24.0 ? 16 : (avg <= 96.0 ? 64 : 128);
+  const int bn = (bm == 16 && !fp8) ? 64 : 128;
+  L.gu = TileShape{bm, bn};
+  L.dn = TileShape{bm, bn};
+  L.router = TileShape{T <= 2048 ? 16 : 64, 64};
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  L.logits = take(T * E * 4);
+  L.topk_idx = take(T * k * 4);
+  L.topk_w = take(T * k * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.perm = take(R * 4);
+  L.inv = take(R * 4);
+  L.chunk_counts = take(static_cast<size_t>(L.nchunks) * E * 4);
+  L.chunk_base = take(static_cast<size_t>(L.nchunks) * E * 4);
+  L.groups = take((E + S) * sizeof(GroupDesc));
+  L.totals = take(16);
+  L.xq = take(fp8 ? T * H : 0);
+  L.xs = take(fp8 ? T * (H / kQBlock) * 4 : 0);
+  L.h = take(rows_all * I * (fp8 ? 1 : asz));
+  L.hs = take(fp8 ? rows_all * (I / kQBlock) * 4 : 0);
+  L.y = take(R * H * asz);
+  L.ysh = take(S * T * H * asz);
+  L.total = off;
+  return L;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK: success";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: null/misaligned pointer or bad size";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: valid configuration this library does not support";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch or API call failed";
+  }
+  return "unknown moe_status_t";
+}
+
+const char* moe_version(void) { return "moe-gfx950 1.0"; }
+
+size_t moe_workspace_size(const moe_config_t* cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  return make_layout(*cfg).total;
+}
+
+moe_status_t moe_route(const moe_config_t* cfg, const void* x, const moe_weights_t* w,
+                       int32_t* topk_idx, float* topk_w, int32_t* tie_counts, void* workspace,
+                       size_t workspace_bytes, moe_stream_t stream) {
+  moe_status_t s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(*cfg, w, true, false)) != MOE_OK) return s;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !aligned16(x) || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  if ((s = check_ws(*cfg, workspace, workspace_bytes)) != MOE_OK) return s;
+  const Layout L = make_layout(*cfg);
+  return hip_status(run_route(*cfg, L, x, *w, topk_idx, topk_w, tie_counts, workspace,
+                              static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* inv, void* workspace,
+                          size_t workspace_bytes, moe_stream_t stream) {
+  moe_status_t s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->T == 0) return MOE_OK;
+  if (!topk_idx || !counts || !offsets || !perm || !inv) return MOE_ERR_INVALID_ARG;
+  if ((s = check_ws(*cfg, workspace, workspace_bytes)) != MOE_OK) return s;
+  const Layout L = make_layout(*cfg);
+  const moe_config_t& c = *cfg;
+  return hip_status(launch_dispatch(topk_idx, c.T, c.k, c.E, c.S,
+                                    at<int32_t>(workspace, L.chunk_counts),
+                                    at<int32_t>(workspace, L.chunk_base), L.nchunks, counts,
+                                    offsets, perm, inv, nullptr, nullptr, L.gu, L.dn, nullptr,
+                                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                    c.H, c.I, expert_kind(c), static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_expert_gate_up(const moe_config_t* cfg, const void* x, const moe_weights_t* w,
+                                const int32_t* perm, const int32_t* offsets, void* workspace,
+                                size_t workspace_bytes, moe_stream_t stream) {
+  moe_status_t s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(*cfg, w, false, true)) != MOE_OK) return s;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !aligned16(x) || !perm || !offsets) return MOE_ERR_INVALID_ARG;
+  if ((s = check_ws(*cfg, workspace, workspace_bytes)) != MOE_OK) return s;
+  const Layout L = make_layout(*cfg);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = run_groups(*cfg, L, offsets, *w, workspace, st);
+  if (e == hipSuccess) e = run_gate_up(*cfg, L, x, perm, workspace, st);
+  return hip_status(e);
+}
+
+moe_status_t moe_expert_down(const moe_config_t* cfg, const moe_weights_t* w, void* y_sorted,
+                             void* y_shared, void* workspace, size_t workspace_bytes,
+                             moe_stream_t stream) {
+  moe_status_t s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(*cfg, w, false, true)) != MOE_OK) return s;
+  if (cfg->T == 0) return MOE_OK;
+  if (!y_sorted || !aligned16(y_sorted)) return MOE_ERR_INVALID_ARG;
+  if (cfg->S > 0 && (!y_shared || !aligned16(y_shared))) return MOE_ERR_INVALID_ARG;
+  if ((s = check_ws(*cfg, workspace, workspace_bytes)) != MOE_OK) return s;
+  const Layout L = make_layout(*cfg);
+  return hip_status(run_down(*cfg, L, y_sorted, y_shared, workspace,
+                             static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_grouped_ffn(const moe_config_t* cfg, const void* x, const moe_weights_t* w,
+                             const int32_t* perm, const int32_t* offsets, void* y_sorted,
+                             void* y_shared, void* workspace, size_t workspace_bytes,
+                             moe_stream_t stream) {
+  moe_status_t s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(*cfg, w, false, true)) != MOE_OK) return s;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !aligned16(x) || !perm || !offsets || !y_sorted || !aligned16(y_sorted))
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->S > 0 && (!y_shared || !aligned16(y_shared))) return MOE_ERR_INVALID_ARG;
+  if ((s = check_ws(*cfg, workspace, workspace_bytes)) != MOE_OK) return s;
+  const Layout L = make_layout(*cfg);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = run_groups(*cfg, L, offsets, *w, workspace, st);
+  if (e == hipSuccess) e = run_gate_up(*cfg, L, x, perm, workspace, st);
+  if (e == hipSuccess) e = run_down(*cfg, L, y_sorted, y_shared, workspace, st);
+  return hip_status(e);
+}
+
+moe_status_t moe_combine(const moe_config_t* cfg, const void* y_sorted, const void* y_shared,
+                         const float* topk_w, const int32_t* inv, void* out, moe_stream_t stream) {
+  moe_status_t s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->T == 0) return MOE_OK;
+  if (!y_sorted || !aligned16(y_sorted) || !topk_w || !inv || !out || !aligned16(out))
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->S > 0 && (!y_shared || !aligned16(y_shared))) return MOE_ERR_INVALID_ARG;
+  const moe_config_t& c = *cfg;
+  return hip_status(launch_combine(act_kind(c), y_sorted, y_shared, topk_w, inv, out, c.T, c.H,
+                                   c.k, c.S, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_quantize_fp8(const void* x_bf16, int32_t rows, int32_t cols, uint8_t* q,
+                              float* scales, moe_stream_t stream) {
+  if (rows < 0 || cols <= 0 || cols % kQBlock != 0) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!x_bf16 || !aligned16(x_bf16) || !q || !aligned16(q) || !scales) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quant_rows_fp8(static_cast<const uint16_t*>(x_bf16), rows, cols, q,
+                                          scales, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                               void* out, int32_t* opt_counts, int32_t* opt_tie_counts,
+                               void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  moe_status_t s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(*cfg, w, true, true)) != MOE_OK) return s;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !aligned16(x) || !out || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+  if ((s = check_ws(*cfg, workspace, workspace_bytes)) != MOE_OK) return s;
+  const moe_config_t& c = *cfg;
+  const Layout L = make_layout(c);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = workspace;
+  int32_t* idx = at<int32_t>(ws, L.topk_idx);
+  float* tw = at<float>(ws, L.topk_w);
+  int32_t* counts = opt_counts ? opt_counts : at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm = at<int32_t>(ws, L.perm);
+  int32_t* inv = at<int32_t>(ws, L.inv);
+  void* y = at<char>(ws, L.y);
+  void* ysh = at<char>(ws, L.ysh);
+
+  hipError_t e = run_route(c, L, x, *w, idx, tw, opt_tie_counts, ws, st);
+  if (e == hipSuccess)
+    e = launch_dispatch(idx, c.T, c.k, c.E, c.S, at<int32_t>(ws, L.chunk_counts),
+                        at<int32_t>(ws, L.chunk_base), L.nchunks, counts, offsets, perm, inv,
+                        at<GroupDesc>(ws, L.groups), at<int32_t>(ws, L.totals), L.gu, L.dn,
+                        w->w_gate_up, w->s_gate_up, w->w_down, w->s_down, w->w_sh_gate_up,
+                        w->s_sh_gate_up, w->w_sh_down, w->s_sh_down, c.H, c.I, expert_kind(c), st);
+  if (e == hipSuccess) e = run_gate_up(c, L, x, perm, ws, st);
+  if (e == hipSuccess) e = run_down(c, L, y, ysh, ws, st);
+  if (e == hipSuccess) e = launch_combine(act_kind(c), y, ysh, tw, inv, out, c.T, c.H, c.k, c.S, st);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+// Internal declarations shared by the host entry points and the kernel files
+// of libmoe (gfx950).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "moe.h"
+
+namespace moe {
+
+// Element kinds of GEMM operands and outputs.
+enum Kind : int { K_F32 = 0, K_BF16 = 1, K_FP8 = 2 };
+
+constexpr int kMaxExperts = 512;
+constexpr int kMaxShared = 4;
+constexpr int kMaxTopK = 16;
+constexpr int kQBlock = 128;          // FP8 scale granularity along K
+constexpr int kDispatchChunk = 1024;  // flat (token, slot) pairs per dispatch wave
+constexpr float kTieEps = 1e-6f;
+
+// One GEMM group = one expert (routed e < E, shared E + s) over a contiguous
+// range of rows of the sorted row space.  Rows [0, R) are the routed (token,
+// slot) pairs in expert order (R = T*k); rows R + s*T + t are token t of
+// shared expert s.  Built on the device from the dispatch offsets.
+struct GroupDesc {
+  int32_t row_begin;
+  int32_t rows;
+  int32_t tile_begin_gu;  // first m-tile id of this group in the gate/up GEMM
+  int32_t tile_begin_dn;  // first m-tile id of this group in the down GEMM
+  const void* w_gu;       // [2I, H] weights of this expert
+  const float* s_gu;      // [2I/128, H/128] block scales (FP8) or null
+  const void* w_dn;       // [H, I]
+  const float* s_dn;      // [H/128, I/128] or null
+};
+
+// Per-GEMM tile shapes chosen on the host from the config (no device sync).
+struct TileShape {
+  int bm;  // rows per tile
+  int bn;  // output columns per tile
+};
+
+// Byte offsets of every buffer inside the caller's workspace.
+struct Layout {
+  size_t logits;        // [T, E] fp32
+  size_t topk_idx;      // [T, k] int32
+  size_t topk_w;        // [T, k] fp32
+  size_t counts;        // [E] int32
+  size_t offsets;       // [E + 1] int32
+  size_t perm;          // [T*k] int32
+  size_t inv;           // [T*k] int32
+  size_t chunk_counts;  // [nchunks, E] int32
+  size_t chunk_base;    // [nchunks, E] int32
+  size_t groups;        // [E + S] GroupDesc
+  size_t totals;        // [4] int32: m-tiles of gate/up, m-tiles of down
+  size_t xq;            // FP8: [T, H] e4m3 codes
+  size_t xs;            // FP8: [T, H/128] fp32 scales
+  size_t h;             // [R + S*T, I] act type, or e4m3 codes (FP8)
+  size_t hs;            // FP8: [R + S*T, I/128] fp32 scales
+  size_t y;             // [R, H] act type  (routed expert outputs, sorted)
+  size_t ysh;           // [S, T, H] act type
+  size_t total;
+  int nchunks;
+  TileShape gu, dn, router;
+};
+
+Layout make_layout(const moe_config_t& c);
+
+inline size_t kind_size(int kind) { return kind == K_F32 ? 4 : kind == K_BF16 ? 2 : 1; }
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  All take the caller's stream.
+
+struct GemmLaunch {
+  // schedule
+  const GroupDesc* groups;
+  int num_groups;
+  const int32_t* total_mtiles;  // device scalar: m-tiles over all groups
+  int dual;                     // 1: gate/up GEMM (uses w_gu), 0: down (w_dn)
+  int single_group_rows;        // >0: one implicit group of this many rows
+                                // (router), weights in b_single
+  const void* b_single;
+  int grid_mtiles_upper;        // host upper bound of m-tiles
+  // shapes
+  int N;  // output columns (h columns for the gate/up GEMM)
+  int K;  // reduction length
+  // A operand
+  const void* A;
+  long long lda;           // elements
+  const float* a_scale;    // FP8: [rows of A, K/128]
+  const int32_t* perm;     // gather: A row of sorted row p < R is perm[p] / k
+  int R, k, T;
+  // outputs
+  void* C;                 // rows [0, c_split)
+  void* C2;                // rows [c_split, ...) at C2 + (row - c_split) * ldc
+  long long c_split;
+  long long ldc;
+  float* c_scale;          // FP8 output scales [rows, N/128]
+};
+
+hipError_t launch_gemm(int a_kind, int out_kind, TileShape ts, const GemmLaunch& g,
+                       hipStream_t st);
+
+hipError_t launch_router_topk(const float* logits, const float* bias, int T, int E, int k,
+                              int norm, float rsf, int32_t* idx, float* w, int32_t* ties,
+                              hipStream_t st);
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t st);
+
+hipError_t launch_dispatch(const int32_t* topk_idx, int T, int k, int E, int S,
+                           int32_t* chunk_counts, int32_t* chunk_base, int nchunks,
+                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                           GroupDesc* groups, int32_t* totals, TileShape gu, TileShape dn,
+                           const void* w_gu, const float* s_gu, const void* w_dn,
+                           const float* s_dn, const void* w_sh_gu, const float* s_sh_gu,
+                           const void* w_sh_dn, const float* s_sh_dn, int H, int I,
+                           int expert_kind, hipStream_t st);
+
+hipError_t launch_groups_only(const int32_t* offsets, int T, int k, int E, int S,
+                              GroupDesc* groups, int32_t* totals, TileShape gu, TileShape dn,
+                              const void* w_gu, const float* s_gu, const void* w_dn,
+                              const float* s_dn, const void* w_sh_gu, const float* s_sh_gu,
+                              const void* w_sh_dn, const float* s_sh_dn, int H, int I,
+                              int expert_kind, hipStream_t st);
+
+hipError_t launch_quant_rows_fp8(const uint16_t* x_bf16, int rows, int cols, uint8_t* q,
+                                 float* scales, hipStream_t st);
+
+hipError_t launch_combine(int act_kind, const void* y, const void* ysh, const float* w,
+                          const int32_t* inv, void* out, int T, int H, int k, int S,
+                          hipStream_t st);
+
+}  // namespace moe

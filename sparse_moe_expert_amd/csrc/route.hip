@@ -1,0 +1,134 @@
+// Router selection: sigmoid scores, bias-for-selection top-k, renormalised
+// weights -- one wavefront per token (gfx950).
+//
+// Scores are sigmoid of the router logits and the choice uses score + bias
+// (noaux_tc), while the weights renormalise the unbiased scores of the k
+// chosen experts (norm_topk_prob): "dots3-note 架构深度解析" (mlqm.cn),
+// «稀疏激活Top-8 路由»; top-k then renormalisation as in the Dots3MoELayer
+// forward of the Deep Dive §3.1; routed_scaling_factor from the Transformers
+// Dots1 article's «MoE 路由与专家相关字段» table.
+//
+// Each lane holds E/64 keys.  A round picks the largest (key, -index) pair of
+// the wave with a 6-step xor-shuffle max over a 64-bit packed key (an
+// order-preserving integer image of the fp32 key in the high half, the
+// complemented expert index in the low half, so equal keys go to the lower
+// index).  k rounds pick the experts in slot order; one more round reads the
+// (k+1)-th key for the near-tie count.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kPer = kMaxExperts / 64;
+
+__device__ __forceinline__ float sigmoidf_acc(float l) { return 1.0f / (1.0f + expf(-l)); }
+
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
+                                                          const float* __restrict__ bias, int T,
+                                                          int E, int k, int norm, float rsf,
+                                                          int32_t* __restrict__ idx_out,
+                                                          float* __restrict__ w_out,
+                                                          int32_t* __restrict__ ties) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave leaves together
+
+  const float* lrow = logits + static_cast<long long>(t) * E;
+  float score[kPer];
+  uint64_t key[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = i * 64 + lane;
+    if (e < E) {
+      score[i] = sigmoidf_acc(lrow[e]);
+      const float c = score[i] + bias[e];
+      key[i] = (static_cast<uint64_t>(f32_order_key(c)) << 32) | static_cast<uint32_t>(~e);
+    } else {
+      score[i] = 0.f;
+      key[i] = 0;  // below every real key
+    }
+  }
+
+  int chosen_e[kMaxTopK];
+  float chosen_s[kMaxTopK];
+  float prev_c = 0.f, min_gap = INFINITY, gap_sel = INFINITY;
+  const int rounds = (k < E) ? k + 1 : k;
+#pragma unroll
+  for (int j = 0; j <= kMaxTopK; ++j) {
+    if (j >= rounds) continue;
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) best = key[i] > best ? key[i] : best;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const uint64_t o = shfl_xor_u64(best, m);
+      best = o > best ? o : best;
+    }
+    const int e = static_cast<int>(~static_cast<uint32_t>(best));
+    const float c = f32_from_order_key(static_cast<uint32_t>(best >> 32));
+    if (j < k) {
+      // the owner lane retires the key and broadcasts the unbiased score
+      float s_own = 0.f;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        if (lane == (e & 63) && i == (e >> 6)) {
+          s_own = score[i];
+          key[i] = 0;
+        }
+      }
+      const float s = __shfl(s_own, e & 63, 64);
+      if (j < kMaxTopK) {
+        chosen_e[j] = e;
+        chosen_s[j] = s;
+      }
+      if (j > 0) min_gap = fminf(min_gap, prev_c - c);
+    } else {
+      gap_sel = prev_c - c;
+    }
+    prev_c = c;
+  }
+
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < k) sum += chosen_s[j];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < k && lane == j) {
+      const float w = norm ? (chosen_s[j] / sum) * rsf : chosen_s[j] * rsf;
+      idx_out[static_cast<long long>(t) * k + j] = chosen_e[j];
+      w_out[static_cast<long long>(t) * k + j] = w;
+    }
+  }
+  if (ties && lane == 0) {
+    if (gap_sel <= kTieEps) atomicAdd(&ties[0], 1);
+    if (min_gap <= kTieEps) atomicAdd(&ties[1], 1);
+  }
+}
+
+__global__ void zero_i32_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_router_topk(const float* logits, const float* bias, int T, int E, int k,
+                              int norm, float rsf, int32_t* idx, float* w, int32_t* ties,
+                              hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  const int waves_per_block = 4;
+  const int grid = (T + waves_per_block - 1) / waves_per_block;
+  hipLaunchKernelGGL(router_topk_kernel, dim3(grid), dim3(64 * waves_per_block), 0, st, logits,
+                     bias, T, E, k, norm, rsf, idx, w, ties);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,156 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, the ctypes structs match the C layout, and host-side
+validation rejects bad calls before anything reaches the device."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+moe = pytest.importorskip("sparse_moe_expert_amd._lib",
+                          reason="libmoe.so not built (python -m sparse_moe_expert_amd.build)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text))
+
+
+def test_exports_match_header():
+    declared = declared_functions()
+    assert declared == set(moe.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (moe_[a-z0-9_]+)$", out, flags=re.M))
+    assert declared <= exported, declared - exported
+    for name in declared:
+        assert getattr(moe.LIB, name) is not None
+
+
+def test_struct_layout_matches_c():
+    src = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "moe.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(moe_config_t), offsetof(moe_config_t, routed_scaling_factor),
+         offsetof(moe_config_t, expert_dtype), sizeof(moe_weights_t),
+         offsetof(moe_weights_t, s_gate_up), offsetof(moe_weights_t, s_sh_down));
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "probe.c")
+        exe = os.path.join(d, "probe")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        vals = list(map(int, subprocess.run([exe], capture_output=True, text=True,
+                                            check=True).stdout.split()))
+    C, W = moe.moe_config_t, moe.moe_weights_t
+    assert vals == [ctypes.sizeof(C), C.routed_scaling_factor.offset, C.expert_dtype.offset,
+                    ctypes.sizeof(W), W.s_gate_up.offset, W.s_sh_down.offset]
+
+
+def test_status_strings_and_version():
+    for code in (0, -1, -2, -3, -4):
+        assert moe.status_string(code).startswith("MOE_")
+    assert "unknown" in moe.status_string(7)
+    assert moe.version().startswith("moe-gfx950")
+
+
+def cfg(**kw):
+    base = dict(T=64, H=512, E=32, S=1, k=4, I=128, act="f32", expert="f32")
+    base.update(kw)
+    return moe.make_config(**base)
+
+
+@pytest.mark.parametrize("kw,ok", [
+    (dict(), True),
+    (dict(act="bf16", expert="bf16"), True),
+    (dict(act="bf16", expert="fp8"), True),
+    (dict(T=0), True),
+    (dict(E=0), False), (dict(k=0), False), (dict(k=33), False), (dict(E=513, k=4), False),
+    (dict(k=17, E=64), False), (dict(H=500), False), (dict(I=100), False), (dict(S=5), False),
+    (dict(I_shared=256), False), (dict(act="f32", expert="bf16"), False),
+    (dict(act="bf16", expert="f32"), False), (dict(T=-1), False),
+])
+def test_workspace_size_validates(kw, ok):
+    n = moe.moe_workspace_size(cfg(**kw))
+    assert (n > 0) == ok
+
+
+def test_workspace_size_covers_buffers():
+    c = moe.make_config(T=16384, H=5120, E=256, S=1, k=8, I=1536)
+    n = moe.moe_workspace_size(c)
+    R = 16384 * 8
+    need = (R + 16384) * 1536 * 2 + R * 5120 * 2 + 16384 * 5120 * 2 + 16384 * 256 * 4
+    assert need <= n < need * 1.05
+
+
+FAKE = 1 << 20   # an aligned, never-dereferenced address: every call below fails validation
+
+
+def weights(**kw):
+    base = dict(w_router=FAKE, router_bias=FAKE, w_gate_up=FAKE, w_down=FAKE,
+                w_sh_gate_up=FAKE, w_sh_down=FAKE)
+    base.update(kw)
+    return moe.make_weights(**base)
+
+
+def call(name, *args):
+    return getattr(moe.LIB, name)(*args)
+
+
+def test_validation_rejects_before_launch():
+    c = cfg()
+    w = weights()
+    by = ctypes.byref
+    n = moe.moe_workspace_size(c)
+    # null config / weights
+    assert call("moe_route", None, FAKE, by(w), FAKE, FAKE, None, FAKE, n, None) == moe.MOE_ERR_INVALID_ARG
+    assert call("moe_layer_forward", by(c), None, FAKE, FAKE, None, None, FAKE, n, None) == moe.MOE_ERR_INVALID_ARG
+    # null / misaligned tensors
+    assert call("moe_route", by(c), None, by(w), FAKE, FAKE, None, FAKE, n, None) == moe.MOE_ERR_INVALID_ARG
+    assert call("moe_route", by(c), FAKE + 4, by(w), FAKE, FAKE, None, FAKE, n, None) == moe.MOE_ERR_INVALID_ARG
+    assert call("moe_layer_forward", by(c), by(weights(w_down=None)), FAKE, FAKE, None, None,
+                FAKE, n, None) == moe.MOE_ERR_INVALID_ARG
+    # workspace missing, misaligned or too small
+    assert call("moe_layer_forward", by(c), by(w), FAKE, FAKE, None, None, None, n, None) == moe.MOE_ERR_WORKSPACE
+    assert call("moe_layer_forward", by(c), by(w), FAKE, FAKE, None, None, FAKE + 16, n, None) == moe.MOE_ERR_WORKSPACE
+    assert call("moe_layer_forward", by(c), by(w), FAKE, FAKE, None, None, FAKE, n - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert call("moe_grouped_ffn", by(c), FAKE, by(w), FAKE, FAKE, FAKE, FAKE, FAKE, n - 256, None) == moe.MOE_ERR_WORKSPACE
+    # unsupported shapes
+    bad = cfg(H=640 + 64)
+    assert call("moe_layer_forward", by(bad), by(w), FAKE, FAKE, None, None, FAKE, n, None) == moe.MOE_ERR_UNSUPPORTED
+    # fp8 needs its block scales
+    c8 = cfg(act="bf16", expert="fp8")
+    n8 = moe.moe_workspace_size(c8)
+    assert call("moe_layer_forward", by(c8), by(w), FAKE, FAKE, None, None, FAKE, n8, None) == moe.MOE_ERR_INVALID_ARG
+    # combine / dispatch / quantiser argument checks
+    assert call("moe_combine", by(c), FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert call("moe_dispatch", by(c), FAKE, None, FAKE, FAKE, FAKE, FAKE, n, None) == moe.MOE_ERR_INVALID_ARG
+    assert call("moe_quantize_fp8", FAKE, 4, 100, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert call("moe_quantize_fp8", FAKE + 8, 4, 128, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_zero_tokens_is_a_noop():
+    """T = 0 returns success without touching the device (no GPU here)."""
+    c = cfg(T=0)
+    w = weights()
+    by = ctypes.byref
+    assert call("moe_layer_forward", by(c), by(w), FAKE, FAKE, None, None, None, 0, None) == moe.MOE_OK
+    assert call("moe_route", by(c), None, by(w), None, None, None, None, 0, None) == moe.MOE_OK
+    assert call("moe_quantize_fp8", None, 0, 128, None, None, None) == moe.MOE_OK
+
+
+def test_python_binding_raises_moe_error():
+    c = cfg(E=0)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_combine(c, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
