@@ -23,7 +23,8 @@
  * Conventions for every entry point:
  *  - All tensor arguments are DEVICE pointers owned by the caller, row-major,
  *    16-byte aligned.  The library never allocates, frees, synchronises or
- *    copies to the host; it holds no mutable global state.
+ *    copies to the host; it holds no mutable global state (only the
+ *    thread-local text of the last HIP error, see moe_last_error_detail).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
  *  - Arguments are validated on the host before anything is enqueued; on an
  *    error nothing is enqueued and no output is touched.  Launch failures
@@ -106,6 +107,11 @@ typedef struct moe_weights {
 /* Human-readable text of a status code (static storage). */
 const char* moe_status_string(moe_status_t status);
 
+/* Text of the HIP error behind the most recent MOE_ERR_HIP returned on the
+ * calling thread ("" if none).  Diagnostic only; the one piece of state the
+ * library keeps, and it is thread-local. */
+const char* moe_last_error_detail(void);
+
 /* Library version string, e.g. "moe-gfx950 1.0". */
 const char* moe_version(void);
 
@@ -147,14 +153,15 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx, int3
  * "gmm1 -> swiglu -> gmm2"].  For sorted row p of expert e (offsets[e] <= p <
  * offsets[e+1]) and its token t = perm[p] / k:
  *   h = SiLU(Wg_e x_t) * (Wu_e x_t),  SiLU(z) = z / (1 + exp(-z))
- *   y_sorted[p] = Wd_e h                                  act_dtype [T*k, H]
+ *   y_sorted[p] = Wd_e h                                  fp32 [T*k, H]
  * and for every shared expert s and token t:
- *   y_shared[s, t] = Wd_s (SiLU(Wg_s x_t) * (Wu_s x_t))   act_dtype [S, T, H]
+ *   y_shared[s, t] = Wd_s (SiLU(Wg_s x_t) * (Wu_s x_t))   fp32 [S, T, H]
  * fp32 accumulation; h is rounded to the activation type (bf16) between the
- * two GEMMs.  FP8: x and h are quantised per token per 128 channels to e4m3
- * with scale amax/448 (fp32) before their GEMM; weights use their block
- * scales.  perm and offsets are moe_dispatch outputs (device).  Workspace:
- * h and the tile schedule. */
+ * two GEMMs; y stays fp32 so that the layer output is rounded only once, in
+ * moe_combine.  FP8: x and h are quantised per token per 128 channels to e4m3
+ * with scale amax/448 (fp32, see moe_quantize_fp8) before their GEMM; weights
+ * use their block scales.  perm and offsets are moe_dispatch outputs (device).
+ * Workspace: h and the tile schedule. */
 moe_status_t moe_grouped_ffn(const moe_config_t* cfg, const void* x, const moe_weights_t* w,
                              const int32_t* perm, const int32_t* offsets, void* y_sorted,
                              void* y_shared, void* workspace, size_t workspace_bytes,
@@ -172,6 +179,7 @@ moe_status_t moe_expert_down(const moe_config_t* cfg, const moe_weights_t* w, vo
 
 /* Combine [DD §3.1 weighted add; §3.3 "Weighted sum" then shared "add"]:
  *   out[t] = Σ_s y_shared[s, t] + Σ_{j=0}^{k-1} topk_w[t, j] * y_sorted[inv[t*k + j]]
+ * y_sorted [T*k, H] and y_shared [S, T, H] are fp32 (moe_grouped_ffn outputs);
  * accumulated in fp32 in exactly this order (s ascending, then j ascending),
  * one rounding to act_dtype.  No atomics.  out [T, H] act_dtype. */
 moe_status_t moe_combine(const moe_config_t* cfg, const void* y_sorted, const void* y_shared,

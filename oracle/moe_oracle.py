@@ -322,7 +322,9 @@ def layer_forward(cfg, inp: dict, tokens=None) -> LayerResult:
     for e in np.unique(r.idx):
         rows, slots = np.nonzero(r.idx == e)
         y[rows, slots] = expert_forward(cfg, x_e[rows], *W.expert(int(e)))
-    ysh = np.stack([expert_forward(cfg, x_e, *W.expert(cfg.E + s)) for s in range(cfg.S)])
+    ysh = np.zeros((cfg.S, n, H))
+    for s in range(cfg.S):
+        ysh[s] = expert_forward(cfg, x_e, *W.expert(cfg.E + s))
     out = ysh.sum(axis=0) + np.einsum("tj,tjh->th", r.w, y)
     return LayerResult(out, r, y, ysh, tokens)
 

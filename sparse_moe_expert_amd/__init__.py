@@ -16,7 +16,7 @@ _BINDING = (
     "make_config", "make_weights", "moe_combine", "moe_config_t", "moe_dispatch",
     "moe_expert_down", "moe_expert_gate_up", "moe_grouped_ffn", "moe_layer_forward",
     "moe_quantize_fp8", "moe_route", "moe_weights_t", "moe_workspace_size", "status_string",
-    "version",
+    "version", "last_error_detail",
 )
 
 __all__ = list(_BINDING)

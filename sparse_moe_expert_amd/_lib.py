@@ -18,7 +18,7 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 
 # every entry point of include/moe.h
-EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route",
+EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_version", "moe_workspace_size", "moe_route",
            "moe_dispatch", "moe_grouped_ffn", "moe_expert_gate_up", "moe_expert_down",
            "moe_combine", "moe_quantize_fp8", "moe_layer_forward")
 
@@ -26,7 +26,9 @@ EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route"
 class MoEError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        detail = LIB.moe_last_error_detail().decode() if status == MOE_ERR_HIP else ""
+        super().__init__(f"{where}: {status_string(status)} (status {status})"
+                         + (f" [{detail}]" if detail else ""))
 
 
 class moe_config_t(ctypes.Structure):
@@ -44,6 +46,11 @@ class moe_weights_t(ctypes.Structure):
 
 
 def _load():
+    # torch ships its own HIP runtime.  Load it first, so that libmoe's
+    # dependency on libamdhip64.so.7 binds to that same runtime instead of
+    # bringing a second one into the process (two runtimes cannot share
+    # device pointers, streams or the device itself).
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libmoe.so not found at {LIB_PATH}; build it with "
                           "`python -m sparse_moe_expert_amd.build` (needs hipcc)")
@@ -54,6 +61,7 @@ def _load():
     sig = {
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_version": (ctypes.c_char_p, []),
+        "moe_last_error_detail": (ctypes.c_char_p, []),
         "moe_workspace_size": (SZ, [CP]),
         "moe_route": (ctypes.c_int, [CP, P, WP, I32P, P, I32P, P, SZ, P]),
         "moe_dispatch": (ctypes.c_int, [CP, I32P, I32P, I32P, I32P, I32P, P, SZ, P]),
@@ -76,6 +84,10 @@ LIB = _load()
 
 def status_string(status: int) -> str:
     return LIB.moe_status_string(status).decode()
+
+
+def last_error_detail() -> str:
+    return LIB.moe_last_error_detail().decode()
 
 
 def version() -> str:

@@ -3,8 +3,9 @@
 // Combine: out[t] = Σ_s y_shared[s, t] + Σ_j w[t, j] * y_sorted[inv[t*k + j]],
 // the weighted sum of the k expert outputs plus the always-on shared expert
 // (Deep Dive §3.1 forward; §3.3 figure "Weighted sum" then "Shared Expert
-// (always) … add").  One workgroup per token gathers its k rows in slot order;
-// fp32 accumulation in a fixed order, one rounding at the store, no atomics.
+// (always) … add").  One workgroup per token gathers its k fp32 rows in slot
+// order; fp32 accumulation in a fixed order, one rounding to the output type
+// at the store, no atomics.
 //
 // Quantisation: per row and 128 channels, scale = amax / 448 (fp32, 1 for an
 // all-zero block) and code = e4m3(v / scale), round to nearest even -- the
@@ -16,14 +17,13 @@
 namespace moe {
 namespace {
 
-template <int AK>
-__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
-                                                      const void* __restrict__ ysh,
+template <int OK>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+                                                      const float* __restrict__ ysh,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ inv,
                                                       void* __restrict__ out, int T, int H, int k,
                                                       int S) {
-  constexpr int VEC = (AK == K_BF16) ? 8 : 4;
   __shared__ float ws[kMaxTopK];
   __shared__ long long rs[kMaxTopK];
   const int t = blockIdx.x;
@@ -32,56 +32,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     rs[threadIdx.x] = inv[static_cast<long long>(t) * k + threadIdx.x];
   }
   __syncthreads();
-  for (int c = threadIdx.x * VEC; c < H; c += blockDim.x * VEC) {
-    float acc[VEC];
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-    if constexpr (AK == K_BF16) {
-      const uint16_t* ysh16 = static_cast<const uint16_t*>(ysh);
-      const uint16_t* y16 = static_cast<const uint16_t*>(y);
-      for (int s = 0; s < S; ++s) {
-        const uint4 v = *reinterpret_cast<const uint4*>(
-            ysh16 + (static_cast<long long>(s) * T + t) * H + c);
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += bf16_to_f32(static_cast<uint16_t>(u[i]));
-          acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(u[i] >> 16));
-        }
-      }
-      for (int j = 0; j < k; ++j) {
-        const float wj = ws[j];
-        const uint4 v = *reinterpret_cast<const uint4*>(y16 + rs[j] * H + c);
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(u[i])), acc[2 * i]);
-          acc[2 * i + 1] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(u[i] >> 16)), acc[2 * i + 1]);
-        }
-      }
-      uint4 o;
-      o.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
-      o.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
-      o.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
-      o.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + static_cast<long long>(t) * H + c) = o;
+  for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
+    float4 acc = float4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(ysh + (static_cast<long long>(s) * T + t) * H + c);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    for (int j = 0; j < k; ++j) {
+      const float wj = ws[j];
+      const float4 v = *reinterpret_cast<const float4*>(y + rs[j] * H + c);
+      acc.x = fmaf(wj, v.x, acc.x);
+      acc.y = fmaf(wj, v.y, acc.y);
+      acc.z = fmaf(wj, v.z, acc.z);
+      acc.w = fmaf(wj, v.w, acc.w);
+    }
+    if constexpr (OK == K_BF16) {
+      uint2 o;
+      o.x = f32_to_bf16(acc.x) | (static_cast<uint32_t>(f32_to_bf16(acc.y)) << 16);
+      o.y = f32_to_bf16(acc.z) | (static_cast<uint32_t>(f32_to_bf16(acc.w)) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + static_cast<long long>(t) * H + c) = o;
     } else {
-      const float* yshf = static_cast<const float*>(ysh);
-      const float* yf = static_cast<const float*>(y);
-      for (int s = 0; s < S; ++s) {
-        const float4 v = *reinterpret_cast<const float4*>(yshf + (static_cast<long long>(s) * T + t) * H + c);
-        acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
-      }
-      for (int j = 0; j < k; ++j) {
-        const float wj = ws[j];
-        const float4 v = *reinterpret_cast<const float4*>(yf + rs[j] * H + c);
-        acc[0] = fmaf(wj, v.x, acc[0]);
-        acc[1] = fmaf(wj, v.y, acc[1]);
-        acc[2] = fmaf(wj, v.z, acc[2]);
-        acc[3] = fmaf(wj, v.w, acc[3]);
-      }
-      *reinterpret_cast<float4*>(static_cast<float*>(out) + static_cast<long long>(t) * H + c) =
-          float4{acc[0], acc[1], acc[2], acc[3]};
+      *reinterpret_cast<float4*>(static_cast<float*>(out) + static_cast<long long>(t) * H + c) = acc;
     }
   }
 }
@@ -127,12 +101,14 @@ hipError_t launch_combine(int act_kind, const void* y, const void* ysh, const fl
                           const int32_t* inv, void* out, int T, int H, int k, int S,
                           hipStream_t st) {
   if (T <= 0) return hipSuccess;
+  const float* yf = static_cast<const float*>(y);
+  const float* yshf = static_cast<const float*>(ysh);
   if (act_kind == K_BF16)
-    hipLaunchKernelGGL(combine_kernel<K_BF16>, dim3(T), dim3(256), 0, st, y, ysh, w, inv, out, T,
-                       H, k, S);
+    hipLaunchKernelGGL(combine_kernel<K_BF16>, dim3(T), dim3(256), 0, st, yf, yshf, w, inv, out,
+                       T, H, k, S);
   else
-    hipLaunchKernelGGL(combine_kernel<K_F32>, dim3(T), dim3(256), 0, st, y, ysh, w, inv, out, T,
-                       H, k, S);
+    hipLaunchKernelGGL(combine_kernel<K_F32>, dim3(T), dim3(256), 0, st, yf, yshf, w, inv, out,
+                       T, H, k, S);
   return hipGetLastError();
 }
 

@@ -436,15 +436,14 @@ hipError_t launch_gemm(int a_kind, int out_kind, TileShape ts, const GemmLaunch&
   if (a_kind == K_F32 && out_kind == K_F32)
     return dual ? launch_shape<K_F32, K_F32, true>(ts, g, st)
                 : launch_shape<K_F32, K_F32, false>(ts, g, st);
-  if (a_kind == K_BF16 && out_kind == K_BF16)
-    return dual ? launch_shape<K_BF16, K_BF16, true>(ts, g, st)
-                : launch_shape<K_BF16, K_BF16, false>(ts, g, st);
+  if (a_kind == K_BF16 && out_kind == K_BF16 && dual)
+    return launch_shape<K_BF16, K_BF16, true>(ts, g, st);
   if (a_kind == K_BF16 && out_kind == K_F32 && !dual)
     return launch_shape<K_BF16, K_F32, false>(ts, g, st);
   if (a_kind == K_FP8 && out_kind == K_FP8 && dual && ts.bn == 128)
     return launch_shape<K_FP8, K_FP8, true>(ts, g, st);
-  if (a_kind == K_FP8 && out_kind == K_BF16 && !dual)
-    return launch_shape<K_FP8, K_BF16, false>(ts, g, st);
+  if (a_kind == K_FP8 && out_kind == K_F32 && !dual)
+    return launch_shape<K_FP8, K_F32, false>(ts, g, st);
   return hipErrorInvalidValue;
 }
 

@@ -79,7 +79,18 @@ moe_status_t check_ws(const moe_config_t& c, void* ws, size_t bytes) {
   return MOE_OK;
 }
 
-moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+thread_local const char* t_last_hip_error = "";
+
+moe_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  t_last_hip_error = hipGetErrorString(e);
+  return MOE_ERR_HIP;
+}
+
+// hipGetLastError() reports the last error of ANY runtime call on this host
+// thread, including the caller's own earlier calls.  Clear it once before our
+// first launch so that the check after each launch sees only that launch.
+void clear_stale_error() { (void)hipGetLastError(); }
 
 template <class T>
 T* at(void* ws, size_t off) {
@@ -177,7 +188,7 @@ hipError_t run_down(const moe_config_t& c, const Layout& L, void* y_sorted, void
   g.C2 = y_shared;
   g.c_split = static_cast<long long>(c.T) * c.k;
   g.ldc = c.H;
-  return launch_gemm(expert_kind(c), act_kind(c), L.dn, g, st);
+  return launch_gemm(expert_kind(c), K_F32, L.dn, g, st);
 }
 
 }  // namespace
@@ -219,8 +230,8 @@ Layout make_layout(const moe_config_t& c) {
   L.xs = take(fp8 ? T * (H / kQBlock) * 4 : 0);
   L.h = take(rows_all * I * (fp8 ? 1 : asz));
   L.hs = take(fp8 ? rows_all * (I / kQBlock) * 4 : 0);
-  L.y = take(R * H * asz);
-  L.ysh = take(S * T * H * asz);
+  L.y = take(R * H * 4);        // fp32: rounded once, in the combine
+  L.ysh = take(S * T * H * 4);
   L.total = off;
   return L;
 }
@@ -244,6 +255,8 @@ const char* moe_status_string(moe_status_t s) {
 
 const char* moe_version(void) { return "moe-gfx950 1.0"; }
 
+const char* moe_last_error_detail(void) { return t_last_hip_error; }
+
 size_t moe_workspace_size(const moe_config_t* cfg) {
   if (check_config(cfg) != MOE_OK) return 0;
   return make_layout(*cfg).total;
@@ -259,6 +272,7 @@ moe_status_t moe_route(const moe_config_t* cfg, const void* x, const moe_weights
   if (!x || !aligned16(x) || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
   if ((s = check_ws(*cfg, workspace, workspace_bytes)) != MOE_OK) return s;
   const Layout L = make_layout(*cfg);
+  clear_stale_error();
   return hip_status(run_route(*cfg, L, x, *w, topk_idx, topk_w, tie_counts, workspace,
                               static_cast<hipStream_t>(stream)));
 }
@@ -273,6 +287,7 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx, int3
   if ((s = check_ws(*cfg, workspace, workspace_bytes)) != MOE_OK) return s;
   const Layout L = make_layout(*cfg);
   const moe_config_t& c = *cfg;
+  clear_stale_error();
   return hip_status(launch_dispatch(topk_idx, c.T, c.k, c.E, c.S,
                                     at<int32_t>(workspace, L.chunk_counts),
                                     at<int32_t>(workspace, L.chunk_base), L.nchunks, counts,
@@ -292,6 +307,7 @@ moe_status_t moe_expert_gate_up(const moe_config_t* cfg, const void* x, const mo
   if ((s = check_ws(*cfg, workspace, workspace_bytes)) != MOE_OK) return s;
   const Layout L = make_layout(*cfg);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  clear_stale_error();
   hipError_t e = run_groups(*cfg, L, offsets, *w, workspace, st);
   if (e == hipSuccess) e = run_gate_up(*cfg, L, x, perm, workspace, st);
   return hip_status(e);
@@ -308,6 +324,7 @@ moe_status_t moe_expert_down(const moe_config_t* cfg, const moe_weights_t* w, vo
   if (cfg->S > 0 && (!y_shared || !aligned16(y_shared))) return MOE_ERR_INVALID_ARG;
   if ((s = check_ws(*cfg, workspace, workspace_bytes)) != MOE_OK) return s;
   const Layout L = make_layout(*cfg);
+  clear_stale_error();
   return hip_status(run_down(*cfg, L, y_sorted, y_shared, workspace,
                              static_cast<hipStream_t>(stream)));
 }
@@ -326,6 +343,7 @@ moe_status_t moe_grouped_ffn(const moe_config_t* cfg, const void* x, const moe_w
   if ((s = check_ws(*cfg, workspace, workspace_bytes)) != MOE_OK) return s;
   const Layout L = make_layout(*cfg);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  clear_stale_error();
   hipError_t e = run_groups(*cfg, L, offsets, *w, workspace, st);
   if (e == hipSuccess) e = run_gate_up(*cfg, L, x, perm, workspace, st);
   if (e == hipSuccess) e = run_down(*cfg, L, y_sorted, y_shared, workspace, st);
@@ -341,6 +359,7 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y_sorted, const vo
     return MOE_ERR_INVALID_ARG;
   if (cfg->S > 0 && (!y_shared || !aligned16(y_shared))) return MOE_ERR_INVALID_ARG;
   const moe_config_t& c = *cfg;
+  clear_stale_error();
   return hip_status(launch_combine(act_kind(c), y_sorted, y_shared, topk_w, inv, out, c.T, c.H,
                                    c.k, c.S, static_cast<hipStream_t>(stream)));
 }
@@ -350,6 +369,7 @@ moe_status_t moe_quantize_fp8(const void* x_bf16, int32_t rows, int32_t cols, ui
   if (rows < 0 || cols <= 0 || cols % kQBlock != 0) return MOE_ERR_INVALID_ARG;
   if (rows == 0) return MOE_OK;
   if (!x_bf16 || !aligned16(x_bf16) || !q || !aligned16(q) || !scales) return MOE_ERR_INVALID_ARG;
+  clear_stale_error();
   return hip_status(launch_quant_rows_fp8(static_cast<const uint16_t*>(x_bf16), rows, cols, q,
                                           scales, static_cast<hipStream_t>(stream)));
 }
@@ -376,6 +396,7 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   void* y = at<char>(ws, L.y);
   void* ysh = at<char>(ws, L.ysh);
 
+  clear_stale_error();
   hipError_t e = run_route(c, L, x, *w, idx, tw, opt_tie_counts, ws, st);
   if (e == hipSuccess)
     e = launch_dispatch(idx, c.T, c.k, c.E, c.S, at<int32_t>(ws, L.chunk_counts),

@@ -59,8 +59,8 @@ struct Layout {
   size_t xs;            // FP8: [T, H/128] fp32 scales
   size_t h;             // [R + S*T, I] act type, or e4m3 codes (FP8)
   size_t hs;            // FP8: [R + S*T, I/128] fp32 scales
-  size_t y;             // [R, H] act type  (routed expert outputs, sorted)
-  size_t ysh;           // [S, T, H] act type
+  size_t y;             // [R, H] fp32  (routed expert outputs, sorted)
+  size_t ysh;           // [S, T, H] fp32
   size_t total;
   int nchunks;
   TileShape gu, dn, router;

