@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer forward on one MI355X (gfx950).
+
+A step is one whole layer forward -- router, dispatch, gate/up + SwiGLU grouped
+GEMM, down grouped GEMM, combine -- over one batch of seeded synthetic input
+already resident in HBM.  Default workload: the prefill-sized dots3-note
+layer (T=16384 tokens, hidden 5120, 256 routed + 1 shared experts, top-8,
+moe_intermediate 1536, bf16).  Prints ONE JSON line on stdout.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Extra objects in the line:
+  roofline     the gate/up GEMM (the dominant kernel), timed live with HIP
+               events recorded on the stream it runs on, against the dense
+               bf16 MFMA peak; traffic from the committed rocprofv3 counter
+               summary when its kernel source hash still matches.
+  decode_T256  the same layer at T=256 tokens (weight streaming): time,
+               algorithmic HBM GB/s and its fraction of 8 TB/s.
+  cpu_baseline the fp64 CPU oracle on the first tokens of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+METRIC = "MoE layer fwd tokens/s & TFLOP/s (T=16384); HBM GB/s at T=256; % roofline"
+GEMM_SRC = os.path.join(ROOT, "sparse_moe_expert_amd", "csrc", "gemm.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def gemm_source_hash() -> str:
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+
+
+def gate_up_flops(cfg) -> float:
+    """Matmul flops of the gate/up GEMM: every routed (token, slot) row and
+    every shared row multiplies [H] by the packed [2I, H] weight."""
+    rows = cfg.T * cfg.k + cfg.T * cfg.S
+    return 2.0 * rows * cfg.H * 2 * cfg.I
+
+
+def weight_bytes_per_expert(cfg) -> float:
+    esz = {"bf16": 2, "f32": 4, "fp8": 1}[cfg.expert]
+    b = 3.0 * cfg.H * cfg.I * esz
+    if cfg.expert == "fp8":
+        b += 4.0 * (2 * cfg.I // 128 * cfg.H // 128 + cfg.H // 128 * cfg.I // 128)
+    return b
+
+
+def layer_bytes(cfg, counts) -> float:
+    """Algorithmic HBM bytes of one layer forward: the weights of every expert
+    that receives a token, the shared experts, the router weight and bias, x in
+    and out; intermediates (h, y) excluded -- the method does not need them."""
+    asz = {"bf16": 2, "f32": 4}[cfg.act]
+    touched = int((counts > 0).sum())
+    return (touched * weight_bytes_per_expert(cfg) + cfg.S * weight_bytes_per_expert(cfg)
+            + cfg.E * cfg.H * asz + 4.0 * cfg.E + 2.0 * cfg.T * cfg.H * asz
+            + 8.0 * cfg.T * cfg.k)
+
+
+def load_traffic(workload: str):
+    """Per-launch HBM bytes of the gate/up GEMM from the committed counter
+    summary, or None if missing or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"gate_up_gemm_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def time_layer(lay, steps, warmup, timed_events=True):
+    import torch
+    import sparse_moe_expert_amd as moe
+    out = lay.empty_out()
+    counts = torch.empty(lay.cfg.E, dtype=torch.int32, device="cuda")
+    for _ in range(warmup):
+        lay.forward(out=out, counts=counts)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    for row in ev:          # torch creates the HIP event on its first record
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        moe.moe_layer_forward_timed(lay.ccfg, lay.weights, lay.t["x"], out, ev[i],
+                                    opt_counts=counts, workspace=lay.workspace)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["route", "dispatch", "quant_x", "gate_up_gemm", "down_gemm", "combine"]
+    stage = {n: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps
+             for j, n in enumerate(names)}
+    step_ev = sum(ev[i][0].elapsed_time(ev[i][6]) for i in range(steps)) / steps
+    return wall * 1e3 / steps, step_ev, stage, counts.cpu().numpy()
+
+
+def cpu_baseline(cfg, inp, n_tokens):
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    tokens = np.arange(min(n_tokens, cfg.T))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.layer_forward(cfg, inp, tokens=tokens)
+        dt = time.perf_counter() - t0
+    return {"value": round(tokens.size / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"first {tokens.size} tokens of {cfg.name} (full routing over all "
+                      f"{cfg.E} experts, their SwiGLU experts and the shared expert), fp64 numpy, "
+                      "one thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload id (default 2: T=16384)")
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-decode", action="store_true", help="skip the T=256 line")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=24)
+    ap.add_argument("--calib-copy-gib", type=float, default=0.0,
+                    help="also run one plain device-to-device copy of this many GiB "
+                         "(calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the layer would shard by experts across GPUs, which is not built here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from moe_inputs import config, generate
+    from sparse_moe_expert_amd.device import DeviceLayer
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = config(args.config)
+    log(f"bench: generating {cfg.name} inputs")
+    t0 = time.perf_counter()
+    inp = generate(cfg)
+    log(f"bench: generated in {time.perf_counter() - t0:.1f}s; uploading")
+    lay = DeviceLayer(cfg, inp)
+    torch.cuda.synchronize()
+
+    log(f"bench: {args.warmup} warmup + {args.steps} timed steps")
+    ms, ms_ev, stage, counts = time_layer(lay, args.steps, args.warmup)
+    flops = cfg.flops()
+    dtype = cfg.expert if cfg.expert != "f32" else "f32"
+    res = {
+        "metric": METRIC,
+        "value": round(cfg.T / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "S": cfg.S,
+                   "k": cfg.k, "I": cfg.I, "precision": dtype, "seed": 0},
+        "tflops": round(flops / (ms / 1e3) / 1e12, 2),
+        "frac_of_peak_mfma_whole_step": round(flops / (ms / 1e3) / 1e12 / PEAK_TFLOPS[dtype], 4),
+        "ms_per_step_events": round(ms_ev, 4),
+        "stages_ms": {k: round(v, 4) for k, v in stage.items()},
+        "rows_per_expert": {"max": int(counts.max()), "mean": float(counts.mean()),
+                            "empty": int((counts == 0).sum())},
+    }
+
+    gu_ms = stage["gate_up_gemm"]
+    achieved = gate_up_flops(cfg) / (gu_ms / 1e3) / 1e12
+    traffic = load_traffic(cfg.name)
+    res["roofline"] = {"kernel": "grouped_gemm gate/up + SwiGLU", "bound": "mfma",
+                       "achieved": round(achieved, 1), "peak": PEAK_TFLOPS[dtype],
+                       "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[dtype], 4),
+                       "traffic": traffic, "kernel_ms": round(gu_ms, 4),
+                       "flops_per_launch": gate_up_flops(cfg)}
+
+    if not args.no_decode and args.config == 2:
+        # T = 256 tokens (the decode-sized workload's x, router weight and bias)
+        # through the same resident expert weights: the two workloads share
+        # every shape and weight distribution.
+        cfg1 = config(1)
+        inp1 = generate(cfg1, weights=False)
+        lay1 = _retarget(lay, cfg1, inp1)
+        log(f"bench: decode T={cfg1.T}: {args.decode_steps} steps")
+        ms1, _, stage1, counts1 = time_layer(lay1, args.decode_steps, 5)
+        b1 = layer_bytes(cfg1, counts1)
+        gbs = b1 / (ms1 / 1e3) / 1e9
+        res["decode_T256"] = {
+            "workload": cfg1.name, "ms_per_step": round(ms1, 4),
+            "tokens_per_s": round(cfg1.T / (ms1 / 1e3), 1),
+            "algorithmic_bytes": b1, "hbm_GBps": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "tflops": round(cfg1.flops() / (ms1 / 1e3) / 1e12, 2),
+            "stages_ms": {k: round(v, 4) for k, v in stage1.items()},
+            "experts_touched": int((counts1 > 0).sum()),
+        }
+
+    if args.calib_copy_gib > 0:
+        n = int(args.calib_copy_gib * (1 << 30))
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        res["calib_copy_bytes"] = n
+
+    if not args.no_cpu_baseline:
+        log(f"bench: CPU oracle on {args.cpu_tokens} tokens")
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_tokens)
+    else:
+        res["cpu_baseline"] = None
+
+    print(json.dumps(res), flush=True)
+
+
+def _retarget(lay, cfg1, inp1):
+    """A DeviceLayer view with another token batch and router, reusing the
+    resident expert weights of `lay` (same shapes)."""
+    import torch
+
+    from sparse_moe_expert_amd import _lib
+    from sparse_moe_expert_amd.device import to_device
+
+    class View:
+        pass
+
+    v = View()
+    v.cfg = cfg1
+    v.ccfg = _lib.make_config(cfg1.T, cfg1.H, cfg1.E, cfg1.S, cfg1.k, cfg1.I, cfg1.Is,
+                              act=cfg1.act, expert=cfg1.expert)
+    t = dict(lay.t)
+    t["x"] = to_device(inp1["x"], cfg1.act)
+    t["w_router"] = to_device(inp1["w_router"], cfg1.act)
+    t["bias"] = to_device(inp1["bias"], "f32")
+    v.t = t
+    v.weights = _lib.make_weights(
+        w_router=t["w_router"], router_bias=t["bias"], w_gate_up=t["w_gate_up"],
+        w_down=t["w_down"], w_sh_gate_up=t["w_sh_gate_up"], w_sh_down=t["w_sh_down"])
+    v.ws_bytes = _lib.moe_workspace_size(v.ccfg)
+    v.workspace = torch.empty(v.ws_bytes, dtype=torch.uint8, device="cuda")
+    v.act_dtype = lay.act_dtype
+    v.empty_out = lambda: torch.empty((cfg1.T, cfg1.H), dtype=lay.act_dtype, device="cuda")
+
+    def forward(out=None, counts=None, ties=None, stream=None):
+        out = v.empty_out() if out is None else out
+        _lib.moe_layer_forward(v.ccfg, v.weights, t["x"], out, counts, ties, v.workspace, stream)
+        return out
+
+    v.forward = forward
+    return v
+
+
+if __name__ == "__main__":
+    main()

@@ -206,6 +206,21 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
                                void* out, int32_t* opt_counts, int32_t* opt_tie_counts,
                                void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
+/* moe_layer_forward that also records HIP events on `stream` at its stage
+ * boundaries, for timing each stage on the stream it runs on:
+ *   events[0] before the router      events[4] after the gate/up GEMM
+ *   events[1] after the router       events[5] after the down GEMM
+ *   events[2] after dispatch         events[6] after the combine
+ *   events[3] after the FP8 activation quantisation (same point as [2]
+ *             when the experts are not FP8)
+ * events: 7 hipEvent_t (passed as void*) created by the caller.  Same
+ * results and the same launches as moe_layer_forward. */
+moe_status_t moe_layer_forward_timed(const moe_config_t* cfg, const moe_weights_t* w,
+                                     const void* x, void* out, int32_t* opt_counts,
+                                     int32_t* opt_tie_counts, void* workspace,
+                                     size_t workspace_bytes, moe_stream_t stream,
+                                     void* const* events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 # every entry point of include/moe.h
 EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_version", "moe_workspace_size", "moe_route",
            "moe_dispatch", "moe_grouped_ffn", "moe_expert_gate_up", "moe_expert_down",
-           "moe_combine", "moe_quantize_fp8", "moe_layer_forward")
+           "moe_combine", "moe_quantize_fp8", "moe_layer_forward", "moe_layer_forward_timed")
 
 
 class MoEError(RuntimeError):
@@ -71,6 +71,8 @@ def _load():
         "moe_combine": (ctypes.c_int, [CP, P, P, P, I32P, P, P]),
         "moe_quantize_fp8": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32, P, P, P]),
         "moe_layer_forward": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P, SZ, P]),
+        "moe_layer_forward_timed": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P, SZ, P,
+                                                   ctypes.POINTER(ctypes.c_void_p)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -189,3 +191,15 @@ def moe_layer_forward(cfg, weights, x, out, opt_counts=None, opt_tie_counts=None
     _check(LIB.moe_layer_forward(ctypes.byref(cfg), ctypes.byref(weights), _ptr(x), _ptr(out),
                                  _ptr(opt_counts), _ptr(opt_tie_counts), wp, wb, _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_layer_forward_timed(cfg, weights, x, out, events, opt_counts=None, opt_tie_counts=None,
+                            workspace=None, stream=None):
+    """events: 7 torch.cuda.Event(enable_timing=True) objects (or raw hipEvent_t ints)."""
+    if len(events) != 7:
+        raise ValueError("moe_layer_forward_timed needs 7 events")
+    arr = (ctypes.c_void_p * 7)(*[e if isinstance(e, int) else e.cuda_event for e in events])
+    wp, wb = _ws(workspace)
+    _check(LIB.moe_layer_forward_timed(ctypes.byref(cfg), ctypes.byref(weights), _ptr(x),
+                                       _ptr(out), _ptr(opt_counts), _ptr(opt_tie_counts), wp, wb,
+                                       _stream(stream), arr), "moe_layer_forward_timed")

@@ -135,14 +135,16 @@ hipError_t run_groups(const moe_config_t& c, const Layout& L, const int32_t* off
                             w.s_sh_down, c.H, c.I, expert_kind(c), st);
 }
 
-hipError_t run_gate_up(const moe_config_t& c, const Layout& L, const void* x, const int32_t* perm,
-                       void* ws, hipStream_t st) {
+hipError_t run_quant_x(const moe_config_t& c, const Layout& L, const void* x, void* ws,
+                       hipStream_t st) {
+  if (!is_fp8(c)) return hipSuccess;
+  return launch_quant_rows_fp8(static_cast<const uint16_t*>(x), c.T, c.H, at<uint8_t>(ws, L.xq),
+                               at<float>(ws, L.xs), st);
+}
+
+hipError_t run_gate_up_gemm(const moe_config_t& c, const Layout& L, const void* x,
+                            const int32_t* perm, void* ws, hipStream_t st) {
   const bool fp8 = is_fp8(c);
-  if (fp8) {
-    hipError_t e = launch_quant_rows_fp8(static_cast<const uint16_t*>(x), c.T, c.H,
-                                         at<uint8_t>(ws, L.xq), at<float>(ws, L.xs), st);
-    if (e != hipSuccess) return e;
-  }
   GemmLaunch g{};
   g.groups = at<GroupDesc>(ws, L.groups);
   g.num_groups = c.E + c.S;
@@ -164,6 +166,69 @@ hipError_t run_gate_up(const moe_config_t& c, const Layout& L, const void* x, co
   g.ldc = c.I;
   g.c_scale = fp8 ? at<float>(ws, L.hs) : nullptr;
   return launch_gemm(expert_kind(c), fp8 ? K_FP8 : act_kind(c), L.gu, g, st);
+}
+
+hipError_t run_gate_up(const moe_config_t& c, const Layout& L, const void* x, const int32_t* perm,
+                       void* ws, hipStream_t st) {
+  hipError_t e = run_quant_x(c, L, x, ws, st);
+  if (e == hipSuccess) e = run_gate_up_gemm(c, L, x, perm, ws, st);
+  return e;
+}
+
+hipError_t run_down(const moe_config_t& c, const Layout& L, void* y_sorted, void* y_shared,
+                    void* ws, hipStream_t st);
+
+hipError_t record(void* const* events, int i, hipStream_t st) {
+  if (!events) return hipSuccess;
+  return hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
+}
+
+// The whole layer; `events` (7 or null) are recorded at the stage boundaries.
+moe_status_t layer_impl(const moe_config_t* cfg, const moe_weights_t* w, const void* x, void* out,
+                        int32_t* opt_counts, int32_t* opt_tie_counts, void* workspace,
+                        size_t workspace_bytes, moe_stream_t stream, void* const* events) {
+  moe_status_t s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(*cfg, w, true, true)) != MOE_OK) return s;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !aligned16(x) || !out || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+  if ((s = check_ws(*cfg, workspace, workspace_bytes)) != MOE_OK) return s;
+  if (events)
+    for (int i = 0; i < 7; ++i)
+      if (!events[i]) return MOE_ERR_INVALID_ARG;
+  const moe_config_t& c = *cfg;
+  const Layout L = make_layout(c);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = workspace;
+  int32_t* idx = at<int32_t>(ws, L.topk_idx);
+  float* tw = at<float>(ws, L.topk_w);
+  int32_t* counts = opt_counts ? opt_counts : at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm = at<int32_t>(ws, L.perm);
+  int32_t* inv = at<int32_t>(ws, L.inv);
+  void* y = at<char>(ws, L.y);
+  void* ysh = at<char>(ws, L.ysh);
+
+  clear_stale_error();
+  hipError_t e = record(events, 0, st);
+  if (e == hipSuccess) e = run_route(c, L, x, *w, idx, tw, opt_tie_counts, ws, st);
+  if (e == hipSuccess) e = record(events, 1, st);
+  if (e == hipSuccess)
+    e = launch_dispatch(idx, c.T, c.k, c.E, c.S, at<int32_t>(ws, L.chunk_counts),
+                        at<int32_t>(ws, L.chunk_base), L.nchunks, counts, offsets, perm, inv,
+                        at<GroupDesc>(ws, L.groups), at<int32_t>(ws, L.totals), L.gu, L.dn,
+                        w->w_gate_up, w->s_gate_up, w->w_down, w->s_down, w->w_sh_gate_up,
+                        w->s_sh_gate_up, w->w_sh_down, w->s_sh_down, c.H, c.I, expert_kind(c), st);
+  if (e == hipSuccess) e = record(events, 2, st);
+  if (e == hipSuccess) e = run_quant_x(c, L, x, ws, st);
+  if (e == hipSuccess) e = record(events, 3, st);
+  if (e == hipSuccess) e = run_gate_up_gemm(c, L, x, perm, ws, st);
+  if (e == hipSuccess) e = record(events, 4, st);
+  if (e == hipSuccess) e = run_down(c, L, y, ysh, ws, st);
+  if (e == hipSuccess) e = record(events, 5, st);
+  if (e == hipSuccess) e = launch_combine(act_kind(c), y, ysh, tw, inv, out, c.T, c.H, c.k, c.S, st);
+  if (e == hipSuccess) e = record(events, 6, st);
+  return hip_status(e);
 }
 
 hipError_t run_down(const moe_config_t& c, const Layout& L, void* y_sorted, void* y_shared,
@@ -377,37 +442,18 @@ moe_status_t moe_quantize_fp8(const void* x_bf16, int32_t rows, int32_t cols, ui
 moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
                                void* out, int32_t* opt_counts, int32_t* opt_tie_counts,
                                void* workspace, size_t workspace_bytes, moe_stream_t stream) {
-  moe_status_t s = check_config(cfg);
-  if (s != MOE_OK) return s;
-  if ((s = check_weights(*cfg, w, true, true)) != MOE_OK) return s;
-  if (cfg->T == 0) return MOE_OK;
-  if (!x || !aligned16(x) || !out || !aligned16(out)) return MOE_ERR_INVALID_ARG;
-  if ((s = check_ws(*cfg, workspace, workspace_bytes)) != MOE_OK) return s;
-  const moe_config_t& c = *cfg;
-  const Layout L = make_layout(c);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  void* ws = workspace;
-  int32_t* idx = at<int32_t>(ws, L.topk_idx);
-  float* tw = at<float>(ws, L.topk_w);
-  int32_t* counts = opt_counts ? opt_counts : at<int32_t>(ws, L.counts);
-  int32_t* offsets = at<int32_t>(ws, L.offsets);
-  int32_t* perm = at<int32_t>(ws, L.perm);
-  int32_t* inv = at<int32_t>(ws, L.inv);
-  void* y = at<char>(ws, L.y);
-  void* ysh = at<char>(ws, L.ysh);
+  return layer_impl(cfg, w, x, out, opt_counts, opt_tie_counts, workspace, workspace_bytes, stream,
+                    nullptr);
+}
 
-  clear_stale_error();
-  hipError_t e = run_route(c, L, x, *w, idx, tw, opt_tie_counts, ws, st);
-  if (e == hipSuccess)
-    e = launch_dispatch(idx, c.T, c.k, c.E, c.S, at<int32_t>(ws, L.chunk_counts),
-                        at<int32_t>(ws, L.chunk_base), L.nchunks, counts, offsets, perm, inv,
-                        at<GroupDesc>(ws, L.groups), at<int32_t>(ws, L.totals), L.gu, L.dn,
-                        w->w_gate_up, w->s_gate_up, w->w_down, w->s_down, w->w_sh_gate_up,
-                        w->s_sh_gate_up, w->w_sh_down, w->s_sh_down, c.H, c.I, expert_kind(c), st);
-  if (e == hipSuccess) e = run_gate_up(c, L, x, perm, ws, st);
-  if (e == hipSuccess) e = run_down(c, L, y, ysh, ws, st);
-  if (e == hipSuccess) e = launch_combine(act_kind(c), y, ysh, tw, inv, out, c.T, c.H, c.k, c.S, st);
-  return hip_status(e);
+moe_status_t moe_layer_forward_timed(const moe_config_t* cfg, const moe_weights_t* w,
+                                     const void* x, void* out, int32_t* opt_counts,
+                                     int32_t* opt_tie_counts, void* workspace,
+                                     size_t workspace_bytes, moe_stream_t stream,
+                                     void* const* events) {
+  if (!events) return MOE_ERR_INVALID_ARG;
+  return layer_impl(cfg, w, x, out, opt_counts, opt_tie_counts, workspace, workspace_bytes, stream,
+                    events);
 }
 
 }  // extern "C"
