@@ -1,0 +1,76 @@
+// Tile schedule shared by the grouped GEMM kernels: the block -> (group,
+// m-tile, n-tile) mapping over the device-built group table.
+#pragma once
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+struct TileJob {
+  int row_begin;   // first row of the group in the sorted row space
+  int m0;          // first row of this tile inside the group
+  int rows_here;   // valid rows in this tile (1..BM)
+  int n0;          // first output column
+  const char* W;   // group weight [N(, 2N), K]
+  const float* WS; // FP8 block scales of W, or null
+};
+
+// Blocks are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8).
+// Remap so that XCD x owns the contiguous run [x * per, (x + 1) * per) of
+// the tile list: consecutive tiles (the n-tiles of one m-tile, the m-tiles of
+// one expert) then share that XCD's L2.  Returns false if the block has no
+// tile.  Tiles are numbered m-tile major, n-tile minor; m-tiles group by group.
+template <int BM, int BN, bool DUAL>
+__device__ __forceinline__ bool find_tile(const GemmLaunch& p, TileJob& job) {
+  const int ntn = (p.N + BN - 1) / BN;
+  const int total_m =
+      p.single_group_rows > 0 ? (p.single_group_rows + BM - 1) / BM : *p.total_mtiles;
+  const int total = total_m * ntn;
+  const int per_xcd = (total + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  if (slot >= per_xcd) return false;
+  const int w_id = (blockIdx.x & 7) * per_xcd + slot;
+  if (w_id >= total) return false;
+  const int mt = w_id / ntn;
+  const int nt = w_id - mt * ntn;
+  int tile_begin;
+  if (p.single_group_rows > 0) {
+    job.row_begin = 0;
+    tile_begin = 0;
+    job.rows_here = p.single_group_rows;
+    job.W = static_cast<const char*>(p.b_single);
+    job.WS = nullptr;
+  } else {
+    int lo = 0, hi = p.num_groups - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      const int tb = DUAL ? p.groups[mid].tile_begin_gu : p.groups[mid].tile_begin_dn;
+      if (tb <= mt) lo = mid; else hi = mid - 1;
+    }
+    const GroupDesc gd = p.groups[lo];
+    job.row_begin = gd.row_begin;
+    job.rows_here = gd.rows;
+    tile_begin = DUAL ? gd.tile_begin_gu : gd.tile_begin_dn;
+    job.W = static_cast<const char*>(DUAL ? gd.w_gu : gd.w_dn);
+    job.WS = DUAL ? gd.s_gu : gd.s_dn;
+  }
+  job.m0 = (mt - tile_begin) * BM;
+  job.rows_here = min(BM, job.rows_here - job.m0);
+  job.n0 = nt * BN;
+  return true;
+}
+
+__device__ __forceinline__ int gemm_a_source_row(const GemmLaunch& p, int row) {
+  if (!p.perm) return row;
+  if (row < p.R) return p.perm[row] / p.k;
+  return (row - p.R) % p.T;
+}
+
+template <int OSZ>
+__device__ __forceinline__ char* gemm_out_row(const GemmLaunch& p, long long row) {
+  if (row < p.c_split) return static_cast<char*>(p.C) + row * p.ldc * OSZ;
+  return static_cast<char*>(p.C2) + (row - p.c_split) * p.ldc * OSZ;
+}
+
+}  // namespace moe

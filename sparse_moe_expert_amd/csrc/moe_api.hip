@@ -272,6 +272,11 @@ Layout make_layout(const moe_config_t& c) {
   const int bn = (bm == 16 && !fp8) ? 64 : 128;
   L.gu = TileShape{bm, bn};
   L.dn = TileShape{bm, bn};
+  if (bm == 128 && c.expert_dtype == MOE_BF16) {
+    // prefill regime: large-tile bf16 kernel (gemm_big.hip)
+    L.gu = TileShape{128, 256};
+    L.dn = TileShape{128, 512};
+  }
   L.router = TileShape{T <= 2048 ? 16 : 64, 64};
 
   size_t off = 0;

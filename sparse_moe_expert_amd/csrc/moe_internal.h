@@ -102,6 +102,10 @@ struct GemmLaunch {
 
 hipError_t launch_gemm(int a_kind, int out_kind, TileShape ts, const GemmLaunch& g,
                        hipStream_t st);
+// Large-tile bf16 kernel (gemm_big.hip): 128 rows x 256 h-columns (gate/up)
+// or 128 rows x 512 output columns (projection).
+bool gemm_big_supported(int a_kind, int out_kind, TileShape ts, bool dual);
+hipError_t launch_gemm_big(int out_kind, bool dual, const GemmLaunch& g, hipStream_t st);
 
 hipError_t launch_router_topk(const float* logits, const float* bias, int T, int E, int k,
                               int norm, float rsf, int32_t* idx, float* w, int32_t* ties,
