@@ -1,0 +1,174 @@
+// Weight-streaming grouped GEMM for the decode regime (a handful of token
+// rows per expert), bf16 operands, fp32 accumulation (gfx950).
+//
+// Same computation as the other grouped GEMM kernels -- gate/up + SwiGLU
+// (gmm1 -> swiglu of the Deep Dive §8.2 figure; packed gate_up per the
+// Transformers Dots1 article «并行策略字段») or a plain projection -- shaped for
+// the HBM roofline: every weight byte of every touched expert is read once,
+// and the rows per expert (about 8 at T=256, top-8 of 256) are too few for
+// any on-chip reuse of the weights to matter.
+//
+//  * One wave owns 16 h-columns (16 gate rows + the 16 matching up rows) or
+//    32 output columns, for 16*MT token rows, over the whole K.  A workgroup
+//    is 4 such waves side by side in N.
+//  * Weights go straight from HBM into registers, no LDS, no barriers: per
+//    128-wide K-block a lane loads 64 contiguous bytes of one weight row
+//    (4 x 16-byte loads), and the next K-block's loads are issued before the
+//    current block's MFMAs.  The MFMA K order is permuted accordingly (lane
+//    group g holds k in [32g, 32g+32) of the block, step s uses its s-th 8),
+//    identically for both operands, which leaves every dot product unchanged.
+//  * The expert's token rows (A) come from L2: all waves of the expert read
+//    the same few rows.
+//  * v_mfma_f32_16x16x32_bf16: rows = tokens (lane%16), columns = weight rows.
+#include "gemm_sched.h"
+
+namespace moe {
+namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int MT, int NT>
+struct Regs {
+  uint4 a[MT][4];
+  uint4 b[NT][4];
+};
+
+template <int MT, bool DUAL>
+__global__ __launch_bounds__(256) void gemm_decode_kernel(GemmLaunch p) {
+  constexpr int BM = 16 * MT;
+  constexpr int BN = DUAL ? 64 : 128;   // output columns per block (4 waves)
+  constexpr int NT = 2;                 // 16-wide weight-row tiles per wave
+  TileJob job;
+  if (!find_tile<BM, BN, DUAL>(p, job)) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lrow = lane & 15;
+  const int lgrp = lane >> 4;
+  const int K = p.K;
+  const int N = p.N;
+  const int nkb = K / 128;
+  const long long rowb_a = p.lda * 2;
+  const long long rowb_b = static_cast<long long>(K) * 2;
+
+  // this wave's weight rows
+  const int wn0 = job.n0 + wave * (DUAL ? 16 : 32);
+  const char* bptr[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    int wr;
+    if constexpr (DUAL) {
+      const int n = min(wn0 + lrow, N - 1);
+      wr = (t == 0) ? n : N + n;  // tile 0 gate rows, tile 1 up rows
+    } else {
+      wr = min(wn0 + t * 16 + lrow, N - 1);
+    }
+    bptr[t] = job.W + wr * rowb_b + lgrp * 64;
+  }
+  const char* aptr[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int r = min(m * 16 + lrow, job.rows_here - 1);
+    const int src = gemm_a_source_row(p, job.row_begin + job.m0 + r);
+    aptr[m] = static_cast<const char*>(p.A) + src * rowb_a + lgrp * 64;
+  }
+
+  auto load = [&](Regs<MT, NT>& R, int kb) {
+    const int off = kb * 256;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) R.b[t][s] = *reinterpret_cast<const uint4*>(bptr[t] + off + s * 16);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) R.a[m][s] = *reinterpret_cast<const uint4*>(aptr[m] + off + s * 16);
+  };
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[m][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Regs<MT, NT>& R) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, R.a[m][s]), __builtin_bit_cast(bf16x8, R.b[t][s]),
+              acc[m][t], 0, 0, 0);
+  };
+
+  Regs<MT, NT> r0, r1;
+  load(r0, 0);
+  int kb = 0;
+  for (; kb + 2 <= nkb; kb += 2) {
+    load(r1, kb + 1);
+    compute(r0);
+    if (kb + 2 < nkb) load(r0, kb + 2);
+    compute(r1);
+  }
+  if (kb < nkb) compute(r0);
+
+  // 16x16 accumulator layout: lane l, element i -> token row 4*(l/16) + i,
+  // weight row l%16 of the tile.
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = m * 16 + lgrp * 4 + i;
+      if (r >= job.rows_here) continue;
+      const long long row = job.row_begin + job.m0 + r;
+      if constexpr (DUAL) {
+        const int n = wn0 + lrow;
+        if (n < N) {
+          const float g = acc[m][0][i];
+          const float u = acc[m][1][i];
+          reinterpret_cast<uint16_t*>(gemm_out_row<2>(p, row))[n] =
+              f32_to_bf16(g / (1.0f + expf(-g)) * u);
+        }
+      } else {
+        float* dst = reinterpret_cast<float*>(gemm_out_row<4>(p, row));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int n = wn0 + t * 16 + lrow;
+          if (n < N) dst[n] = acc[m][t][i];
+        }
+      }
+    }
+}
+
+template <int MT, bool DUAL>
+hipError_t launch_decode(const GemmLaunch& g, hipStream_t st) {
+  constexpr int BM = 16 * MT;
+  constexpr int BN = DUAL ? 64 : 128;
+  const int ntn = (g.N + BN - 1) / BN;
+  const long long ub_m =
+      g.single_group_rows > 0 ? (g.single_group_rows + BM - 1) / BM : g.grid_mtiles_upper;
+  const long long total = ub_m * ntn;
+  if (total <= 0) return hipSuccess;
+  const long long grid = ((total + 7) / 8) * 8;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_decode_kernel<MT, DUAL>), dim3(static_cast<unsigned>(grid)), dim3(256),
+                     0, st, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_decode_supported(int a_kind, int out_kind, TileShape ts, bool dual) {
+  if (a_kind != K_BF16 || (ts.bm != 16 && ts.bm != 32)) return false;
+  if (dual) return out_kind == K_BF16 && ts.bn == 64;
+  return out_kind == K_F32 && ts.bn == 128;
+}
+
+hipError_t launch_gemm_decode(TileShape ts, bool dual, const GemmLaunch& g, hipStream_t st) {
+  if (ts.bm == 16) return dual ? launch_decode<1, true>(g, st) : launch_decode<1, false>(g, st);
+  return dual ? launch_decode<2, true>(g, st) : launch_decode<2, false>(g, st);
+}
+
+}  // namespace moe

@@ -272,10 +272,17 @@ Layout make_layout(const moe_config_t& c) {
   const int bn = (bm == 16 && !fp8) ? 64 : 128;
   L.gu = TileShape{bm, bn};
   L.dn = TileShape{bm, bn};
-  if (bm == 128 && c.expert_dtype == MOE_BF16) {
-    // prefill regime: large-tile bf16 kernel (gemm_big.hip)
-    L.gu = TileShape{128, 256};
-    L.dn = TileShape{128, 512};
+  if (c.expert_dtype == MOE_BF16) {
+    if (avg <= 12.0) {          // decode regime: weight streaming (gemm_decode.hip)
+      L.gu = TileShape{16, 64};
+      L.dn = TileShape{16, 128};
+    } else if (avg <= 24.0) {
+      L.gu = TileShape{32, 64};
+      L.dn = TileShape{32, 128};
+    } else if (bm == 128) {     // prefill regime: large tiles (gemm_big.hip)
+      L.gu = TileShape{128, 256};
+      L.dn = TileShape{128, 512};
+    }
   }
   L.router = TileShape{T <= 2048 ? 16 : 64, 64};
 
