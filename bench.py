@@ -71,6 +71,41 @@ def layer_bytes(cfg, counts) -> float:
             + 8.0 * cfg.T * cfg.k)
 
 
+def gate_up_bytes(cfg, counts) -> float:
+    """Algorithmic HBM bytes of one gate/up GEMM launch: the packed gate/up
+    weights (and block scales) of every touched routed expert and of the
+    shared experts, each token row of x read once, h written once."""
+    esz = {"bf16": 2, "f32": 4, "fp8": 1}[cfg.expert]
+    w = 2.0 * cfg.I * cfg.H * esz
+    if cfg.expert == "fp8":
+        w += 4.0 * (2 * cfg.I // 128) * (cfg.H // 128)
+    touched = int((counts > 0).sum())
+    rows = cfg.T * cfg.k + cfg.T * cfg.S
+    x_b = cfg.T * cfg.H * (1 if cfg.expert == "fp8" else esz)
+    h_b = rows * cfg.I * (1 if cfg.expert == "fp8" else 2)
+    return (touched + cfg.S) * w + x_b + h_b
+
+
+def gate_up_roofline(cfg, ms, counts, dtype):
+    """The dominant kernel against the roof that bounds it: MFMA peak of its
+    dtype when its intensity is above the ridge point, else HBM."""
+    flops = gate_up_flops(cfg)
+    byts = gate_up_bytes(cfg, counts)
+    peak_f = PEAK_TFLOPS[dtype]
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+    traffic = load_traffic(cfg.name)
+    base = {"kernel": "grouped_gemm gate/up + SwiGLU", "kernel_ms": round(ms, 4),
+            "flops_per_launch": flops, "bytes_per_launch": byts,
+            "intensity_flop_per_byte": round(flops / byts, 1), "traffic": traffic}
+    if flops / byts >= ridge:
+        a = flops / (ms / 1e3) / 1e12
+        return dict(base, bound="mfma", achieved=round(a, 1), peak=peak_f, unit="TFLOP/s",
+                    frac=round(a / peak_f, 4))
+    a = byts / (ms / 1e3) / 1e9
+    return dict(base, bound="hbm", achieved=round(a, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                frac=round(a / PEAK_HBM_GBS, 4))
+
+
 def load_traffic(workload: str):
     """Per-launch HBM bytes of the gate/up GEMM from the committed counter
     summary, or None if missing or taken on a different kernel source."""
@@ -189,14 +224,7 @@ def main():
                             "empty": int((counts == 0).sum())},
     }
 
-    gu_ms = stage["gate_up_gemm"]
-    achieved = gate_up_flops(cfg) / (gu_ms / 1e3) / 1e12
-    traffic = load_traffic(cfg.name)
-    res["roofline"] = {"kernel": "grouped_gemm gate/up + SwiGLU", "bound": "mfma",
-                       "achieved": round(achieved, 1), "peak": PEAK_TFLOPS[dtype],
-                       "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[dtype], 4),
-                       "traffic": traffic, "kernel_ms": round(gu_ms, 4),
-                       "flops_per_launch": gate_up_flops(cfg)}
+    res["roofline"] = gate_up_roofline(cfg, stage["gate_up_gemm"], counts, dtype)
 
     if not args.no_decode and args.config == 2:
         # T = 256 tokens (the decode-sized workload's x, router weight and bias)

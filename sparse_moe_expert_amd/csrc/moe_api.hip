@@ -285,6 +285,7 @@ Layout make_layout(const moe_config_t& c) {
     }
   }
   L.router = TileShape{T <= 2048 ? 16 : 64, 64};
+  if (c.act_dtype == MOE_BF16 && T >= 4096) L.router = TileShape{128, 512};  // gemm_big.hip
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
