@@ -34,7 +34,8 @@ if ROOT not in sys.path:
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE layer fwd tokens/s & TFLOP/s (T=16384); HBM GB/s at T=256; % roofline"
-GEMM_SRC = os.path.join(ROOT, "sparse_moe_expert_amd", "csrc", "gemm.hip")
+GEMM_SRCS = [os.path.join(ROOT, "sparse_moe_expert_amd", "csrc", f)
+             for f in ("gemm.hip", "gemm_big.hip", "gemm_decode.hip", "gemm_sched.h")]
 
 
 def log(msg):
@@ -42,7 +43,12 @@ def log(msg):
 
 
 def gemm_source_hash() -> str:
-    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the GEMM kernel sources: counter figures taken on other sources
+    no longer describe the kernel that runs."""
+    h = hashlib.sha256()
+    for f in GEMM_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def gate_up_flops(cfg) -> float:
