@@ -433,7 +433,8 @@ hipError_t launch_shape(TileShape ts, const GemmLaunch& g, hipStream_t st) {
 hipError_t launch_gemm(int a_kind, int out_kind, TileShape ts, const GemmLaunch& g,
                        hipStream_t st) {
   const bool dual = g.dual != 0;
-  if (gemm_big_supported(a_kind, out_kind, ts, dual)) return launch_gemm_big(out_kind, dual, g, st);
+  if (gemm_big_supported(a_kind, out_kind, ts, dual))
+    return launch_gemm_big(a_kind, out_kind, dual, g, st);
   if (gemm_decode_supported(a_kind, out_kind, ts, dual)) return launch_gemm_decode(ts, dual, g, st);
   if (a_kind == K_F32 && out_kind == K_F32)
     return dual ? launch_shape<K_F32, K_F32, true>(ts, g, st)

@@ -1,25 +1,33 @@
 // Large-tile grouped GEMM for the prefill regime (hundreds of rows per
-// expert), bf16 operands, fp32 accumulation (gfx950).
+// expert), bf16 or fp8-e4m3 operands, fp32 accumulation (gfx950).
 //
 // Same computation as the generic kernel in gemm.hip -- gate/up + SwiGLU
 // (gmm1 -> swiglu of the Deep Dive §8.2 figure, SwiGLU with packed gate_up
 // per the Transformers Dots1 article «并行策略字段») or a plain projection --
 // with a tiling chosen for the MFMA roofline:
 //
-//  * A workgroup of 16 waves (4 per SIMD) owns 128 rows x 512 weight rows;
-//    each wave owns 64 rows x 64 weight rows (2 x 2 tiles of
-//    v_mfma_f32_32x32x16_bf16, 64 fp32 accumulators per lane).  Sixteen waves
-//    per CU are what it takes to keep enough loads in flight: measured on
-//    MI355X, streaming throughput per CU grows with the number of issuing
-//    waves (about 27 GB/s with 4, 50 with 8, 78 with 16), not with how deep
-//    one wave's queue is.
-//  * For the gate/up GEMM a wave's 64 weight rows are 32 gate rows and the 32
-//    matching up rows, so SiLU(g) * u is formed in registers.
+//  * A workgroup of 16 waves (4 per SIMD) owns 128 rows x 512 weight rows.
+//    Sixteen waves per CU are what it takes to keep enough loads in flight:
+//    measured on MI355X, streaming throughput per CU grows with the number of
+//    issuing waves (about 27 GB/s with 4, 50 with 8, 78 with 16), not with
+//    how deep one wave's queue is.
+//  * bf16: each wave owns 64 rows x 64 weight rows (2 x 2 tiles of
+//    v_mfma_f32_32x32x16_bf16, 64 fp32 accumulators per lane).
+//  * fp8: each wave owns 32 rows x 128 weight rows (2 x 8 tiles of
+//    v_mfma_scale_f32_16x16x128_f8f6f4, weight rows as the MFMA rows), one
+//    instruction per 128-wide scale block, so the per-block scales (row scale
+//    of the activations times block scale of the weights, DeepSeek-V3
+//    Technical Report, FP8 training section) multiply each partial product
+//    once before it is added to the fp32 accumulators.  The gate/up variant
+//    quantizes h per token and 128 columns in its epilogue.
+//  * For the gate/up GEMM each group of 64 weight rows is 32 gate rows and the
+//    32 matching up rows, so SiLU(g) * u is formed on chip.
 //  * Tiles of A (gathered token rows) and W stream global -> LDS with
 //    global_load_lds_dwordx4 (no register staging), double buffered in
-//    64-wide K-slices (80 KB each; two fill the 160 KB LDS).  One wait and one
-//    fence-free barrier per slice.  16-byte chunks XOR-swizzled by row so the
-//    16 lanes of each LDS read phase hit 16 distinct bank groups.
+//    128-byte K-slices (64 bf16 or 128 e4m3 per row; 80 KB per stage, two
+//    fill the 160 KB LDS).  One wait and one fence-free barrier per slice.
+//    16-byte chunks XOR-swizzled by row so the 16 lanes of each LDS read
+//    phase hit 16 distinct bank groups.
 //  * 128 rows per tile keeps the ragged last tile of each expert (about 512
 //    rows each at T=16384) to ~12% padding.
 #include "gemm_sched.h"
@@ -31,7 +39,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128;
 constexpr int BROWS = 512;               // weight rows per block
-constexpr int KS = 64;                   // bf16 elements per K-slice (128 bytes per row)
+// K-slices are 128 bytes per row: 64 bf16 or 128 e4m3 elements.
 constexpr int NS = 2;                    // K-slices resident in LDS
 constexpr int WAVES = 16;                // 4 per SIMD
 constexpr int THREADS = WAVES * 64;
@@ -77,9 +85,15 @@ __device__ __forceinline__ void barrier_no_fence() {
   __asm__ volatile("" ::: "memory");
 }
 
-template <int OK, bool DUAL>
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(4))) float* const_f32_ptr;
+
+template <int AK, int OK, bool DUAL>
 __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
   constexpr int BN = DUAL ? 256 : 512;  // output columns per block
+  constexpr int ESZ = (AK == K_FP8) ? 1 : 2;
+  constexpr int KE = 128 / ESZ;         // K elements per 128-byte slice
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
 
   TileJob job;
@@ -87,12 +101,13 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave index is uniform across the wave: keep it (and what derives from it) scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = p.K;
-  const int nk = K / KS;
+  const int nk = K / KE;
   const int N = p.N;
-  const long long rowb_a = p.lda * 2;
-  const long long rowb_b = static_cast<long long>(K) * 2;
+  const long long rowb_a = p.lda * ESZ;
+  const long long rowb_b = static_cast<long long>(K) * ESZ;
 
   // DMA group g (8 rows x 128 bytes = 1 KB) fills tile rows g*8 + lane/8 at
   // physical chunk lane%8, which holds logical chunk (lane%8) ^ key(row).
@@ -124,31 +139,99 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
     b_off[i] = static_cast<uint32_t>(wr * rowb_b + lchunk * 16);
   }
 
+  // wave (wm, wn): rows [wm*64, +64) x B-tile rows [wn*64, +64)
+  const int wm = wave >> 3;
+  const int wn = wave & 7;
+  const int lrow = lane & 31;
+  const int lhalf = lane >> 5;
+
+  // FP8 waves form a 4 x 4 grid instead: wave (wm8, wn8) owns tokens
+  // [wm8*32, +32) x B-tile rows [wn8*128, +128), as 2 x 8 tiles of
+  // v_mfma_scale_f32_16x16x128_f8f6f4 with the weight rows as the output
+  // rows.  Each K-slice is one 128-wide scale block, and a lane's 4
+  // accumulators of a tile share one token (its column) and one 128-row
+  // weight block, so each partial product takes a single scale product per
+  // lane: row scale of A times block scale of W.
+  const int wm8 = wave >> 2;
+  const int wn8 = wave & 3;
+  const int r16 = lane & 15;
+  int sa_off[2] = {0, 0};
+  float sa_next[2] = {0.f, 0.f};
+  const int kblocks = K / kQBlock;
+  if constexpr (AK == K_FP8) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int r = min(wm8 * 32 + tt * 16 + r16, job.rows_here - 1);
+      sa_off[tt] = gemm_a_source_row(p, job.row_begin + job.m0 + r) * kblocks;
+    }
+  }
+
+  // FP8 weight block scales of the wave's 128 B-tile rows.  Gate/up: h
+  // columns [n0 + wn8*64, +64), all in one 128-block, [0] its gate block and
+  // [1] its up block.  Projection: output rows [n0 + wn8*128, +128), one block.
+  const float* sb_src[2] = {nullptr, nullptr};
+  if constexpr (AK == K_FP8) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      int wr0;
+      if constexpr (DUAL) wr0 = (q == 0 ? 0 : N) + min(job.n0 + wn8 * 64, N - 1);
+      else wr0 = min(job.n0 + wn8 * 128, N - 1);
+      sb_src[q] = job.WS + static_cast<long long>(wr0 / kQBlock) * kblocks;
+    }
+  }
+  // Weight block scales, loaded with the slice's DMA.  Wave-uniform: scalar loads
+  // through the constant address space (the scales are read-only here), which
+  // keeps them off the vector memory counter that the slice pipeline waits on.
+  float sb_next[2] = {0.f, 0.f};
+  auto load_sb = [&](int kt) {
+    sb_next[0] = ((const_f32_ptr)(sb_src[0]))[kt];
+    sb_next[1] = ((const_f32_ptr)(sb_src[1]))[kt];
+  };
   auto issue = [&](int kt) {
     char* base = smem + (kt % NS) * STAGE;
-    const int koff = kt * (KS * 2);
+    const int koff = kt * 128;
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i) dma16(a_src[i] + koff, base + (i * WAVES + wave) * 1024);
 #pragma unroll
     for (int i = 0; i < B_DMA; ++i)
       dma16(job.W + b_off[i] + koff, base + A_BYTES + (i * WAVES + wave) * 1024);
+    if constexpr (AK == K_FP8) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) sa_next[tt] = p.a_scale[sa_off[tt] + kt];
+      load_sb(kt);
+    }
   };
 
-  // wave (wm, wn): rows [wm*64, +64) x B-tile rows [wn*64, +64)
-  const int wm = wave >> 3;
-  const int wn = wave & 7;
-  f32x16 acc[2][2];
+  // FP8 LDS read offsets of this lane: A-tile row wm8*32 + r16 and B-tile row
+  // wn8*128 + r16 (+16 per tile), logical chunks c0 and c0+1.  Rows 16 apart
+  // share the swizzle key.
+  int x_off0 = 0, x_off1 = 0, w_off0 = 0, w_off1 = 0;
+  if constexpr (AK == K_FP8) {
+    const int c0 = 2 * (lane >> 4);
+    const int key = swz_key(r16);
+    x_off0 = (wm8 * 32 + r16) * 128 + ((c0 ^ key) << 4);
+    x_off1 = (wm8 * 32 + r16) * 128 + (((c0 + 1) ^ key) << 4);
+    w_off0 = (wn8 * 128 + r16) * 128 + ((c0 ^ key) << 4);
+    w_off1 = (wn8 * 128 + r16) * 128 + (((c0 + 1) ^ key) << 4);
+  }
+  f32x16 acc[2][2];   // bf16: 2 x 2 tiles of 32x32
+  f32x4 acc8[8][2];   // fp8: 8 weight tiles x 2 token tiles of 16x16
+  if constexpr (AK == K_FP8) {
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+      for (int b = 0; b < 2; ++b) acc8[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+  }
 
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk) issue(s);
 
-  const int lrow = lane & 31;
-  const int lhalf = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
     // slice kt has landed for this thread once only the slices issued after
     // it (at most NS-2 of them) are outstanding
@@ -159,11 +242,44 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
       wait_vmem<0>();
     }
     barrier_no_fence();  // everyone's slice kt landed; slice kt-1's buffer is free
+    const float sa_cur[2] = {sa_next[0], sa_next[1]};
+    const float sb_cur[2] = {sb_next[0], sb_next[1]};
     if (kt + NS - 1 < nk) issue(kt + NS - 1);
     const char* As = smem + (kt % NS) * STAGE;
     const char* Bs = As + A_BYTES;
+    if constexpr (AK == K_FP8) {
+      // Lane l holds 32 bytes of row l%16: logical chunks 2*(l/16) and
+      // 2*(l/16)+1 of the slice, the same K order for both operands.
+      const float sbg = sb_cur[0];
+      const float sbu = DUAL ? sb_cur[1] : sbg;
+      const float sg[2] = {sa_cur[0] * sbg, sa_cur[1] * sbg};
+      const float su[2] = {sa_cur[0] * sbu, sa_cur[1] * sbu};
+      i32x8_t xf[2];
 #pragma unroll
-    for (int s = 0; s < KS / 16; ++s) {
+      for (int tt = 0; tt < 2; ++tt) {
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(As + x_off0 + tt * 2048);
+        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(As + x_off1 + tt * 2048);
+        xf[tt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int tw = 0; tw < 8; ++tw) {
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(Bs + w_off0 + tw * 2048);
+        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(Bs + w_off1 + tw * 2048);
+        const i32x8_t wf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        // gate/up: tiles with (tw & 2) set are up rows
+        const bool up = DUAL && (tw & 2);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          // cbsz = blgp = 0: both operands e4m3; E8M0 scales 127 = 2^0
+          const f32x4 t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wf, xf[tt], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+          acc8[tw][tt] += t * (up ? su[tt] : sg[tt]);
+        }
+      }
+      continue;
+    }
+#pragma unroll
+    for (int s = 0; s < KE / 16; ++s) {
       const int ch = s * 2 + lhalf;
       bf16x8 a[2], b[2];
 #pragma unroll
@@ -182,8 +298,95 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
 
   // ------------------------------------------------------------ epilogue
   // 32x32 accumulator layout: lane l, element i -> row 8*(i/4) + 4*(l/32) + i%4,
-  // column l%32 of the 32x32 tile.
-  if constexpr (DUAL) {
+  // column l%32 of the 32x32 tile (bf16: rows = tokens, columns = weight rows).
+  if constexpr (AK == K_FP8) {
+    __syncthreads();  // all waves are done with the operand buffers
+    constexpr int LDC = 256 + 4;
+    float* Cs = reinterpret_cast<float*>(smem);
+    if constexpr (DUAL) {
+      // h = SiLU(g) * u into Cs[token][h column], then per token and 128
+      // columns: scale = amax / 448, code = e4m3(h / scale)
+      // 16x16 layout (weight rows as rows): lane l, element i -> weight row
+      // 4*(l/16) + i of the tile, token l%16 of the tile.  B-tile rows
+      // [q*64, +64) are 32 gate rows then the 32 matching up rows, so gate
+      // tile tw (tw & 2 clear) pairs with up tile tw + 2, h column
+      // q*32 + (tw & 1)*16 + row, q = 2*wn8 + tw/4.
+#pragma unroll
+      for (int tw = 0; tw < 8; ++tw) {
+        if (tw & 2) continue;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = wm8 * 32 + tt * 16 + r16;
+            const int c = (2 * wn8 + (tw >> 2)) * 32 + (tw & 1) * 16 + 4 * (lane >> 4) + i;
+            const float g = acc8[tw][tt][i];
+            const float u = acc8[tw + 2][tt][i];
+            Cs[tok * LDC + c] = g / (1.0f + expf(-g)) * u;
+          }
+      }
+      __syncthreads();
+      static_assert(OK == K_FP8, "FP8 gate/up output is e4m3 + scales");
+      for (int q = tid; q < BM * 32; q += THREADS) {
+        const int r = q >> 5;
+        const int c8 = (q & 31) * 8;  // 16 lanes per 128-column block
+        const float* src = Cs + r * LDC + c8;
+        float v[8];
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          v[i] = src[i];
+          amax = fmaxf(amax, fabsf(v[i]));
+        }
+#pragma unroll
+        for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+        const float scale = (amax == 0.f) ? 1.0f : amax / 448.0f;
+        const int n = job.n0 + c8;
+        if (r < job.rows_here && n < N) {
+          const long long row = job.row_begin + job.m0 + r;
+          uint2 codes;
+          codes.x = f32x4_to_e4m3(v[0] / scale, v[1] / scale, v[2] / scale, v[3] / scale);
+          codes.y = f32x4_to_e4m3(v[4] / scale, v[5] / scale, v[6] / scale, v[7] / scale);
+          *reinterpret_cast<uint2*>(gemm_out_row<1>(p, row) + n) = codes;
+          if ((q & 15) == 0) p.c_scale[row * (N / kQBlock) + n / kQBlock] = scale;
+        }
+      }
+    } else {
+      static_assert(OK == K_F32, "FP8 projection output is fp32");
+      // two passes of 256 output columns through Cs[token][column]
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if ((wn8 >> 1) == half) {
+#pragma unroll
+          for (int tw = 0; tw < 8; ++tw)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int tok = wm8 * 32 + tt * 16 + r16;
+                const int c = (wn8 & 1) * 128 + tw * 16 + 4 * (lane >> 4) + i;
+                Cs[tok * LDC + c] = acc8[tw][tt][i];
+              }
+        }
+        __syncthreads();
+        for (int q = tid; q < BM * 64; q += THREADS) {
+          const int r = q >> 6;
+          const int c4 = (q & 63) * 4;
+          const int n = job.n0 + half * 256 + c4;
+          if (r < job.rows_here && n < N) {
+            const float* src = Cs + r * LDC + c4;
+            float* dst = reinterpret_cast<float*>(gemm_out_row<4>(p, job.row_begin + job.m0 + r));
+            if (n + 4 <= N) {
+              *reinterpret_cast<float4*>(dst + n) = float4{src[0], src[1], src[2], src[3]};
+            } else {
+              for (int i = 0; n + i < N; ++i) dst[n + i] = src[i];
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+  } else if constexpr (DUAL) {
     __syncthreads();  // all waves are done with the operand buffers
     constexpr int LDC = 256 + 4;
     float* Cs = reinterpret_cast<float*>(smem);
@@ -236,7 +439,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
   }
 }
 
-template <int OK, bool DUAL>
+template <int AK, int OK, bool DUAL>
 hipError_t launch_big(const GemmLaunch& g, hipStream_t st) {
   constexpr int BN = DUAL ? 256 : 512;
   const int ntn = (g.N + BN - 1) / BN;
@@ -246,22 +449,35 @@ hipError_t launch_big(const GemmLaunch& g, hipStream_t st) {
   if (total <= 0) return hipSuccess;
   const long long grid = ((total + 7) / 8) * 8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_big_kernel<OK, DUAL>), dim3(static_cast<unsigned>(grid)), dim3(THREADS),
-                     0, st, g);
+  hipLaunchKernelGGL((gemm_big_kernel<AK, OK, DUAL>), dim3(static_cast<unsigned>(grid)),
+                     dim3(THREADS), 0, st, g);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool gemm_big_supported(int a_kind, int out_kind, TileShape ts, bool dual) {
-  if (a_kind != K_BF16 || ts.bm != BM) return false;
-  if (dual) return out_kind == K_BF16 && ts.bn == 256;
-  return out_kind == K_F32 && ts.bn == 512;
+  if (ts.bm != BM) return false;
+  if (a_kind == K_BF16) {
+    if (dual) return out_kind == K_BF16 && ts.bn == 256;
+    return out_kind == K_F32 && ts.bn == 512;
+  }
+  if (a_kind == K_FP8) {
+    if (dual) return out_kind == K_FP8 && ts.bn == 256;
+    return out_kind == K_F32 && ts.bn == 512;
+  }
+  return false;
 }
 
-hipError_t launch_gemm_big(int out_kind, bool dual, const GemmLaunch& g, hipStream_t st) {
-  if (dual && out_kind == K_BF16) return launch_big<K_BF16, true>(g, st);
-  if (!dual && out_kind == K_F32) return launch_big<K_F32, false>(g, st);
+hipError_t launch_gemm_big(int a_kind, int out_kind, bool dual, const GemmLaunch& g,
+                           hipStream_t st) {
+  if (a_kind == K_BF16) {
+    if (dual && out_kind == K_BF16) return launch_big<K_BF16, K_BF16, true>(g, st);
+    if (!dual && out_kind == K_F32) return launch_big<K_BF16, K_F32, false>(g, st);
+  } else if (a_kind == K_FP8) {
+    if (dual && out_kind == K_FP8) return launch_big<K_FP8, K_FP8, true>(g, st);
+    if (!dual && out_kind == K_F32) return launch_big<K_FP8, K_F32, false>(g, st);
+  }
   return hipErrorInvalidValue;
 }
 

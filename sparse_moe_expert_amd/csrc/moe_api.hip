@@ -283,6 +283,9 @@ Layout make_layout(const moe_config_t& c) {
       L.gu = TileShape{128, 256};
       L.dn = TileShape{128, 512};
     }
+  } else if (fp8 && bm == 128) {
+    L.gu = TileShape{128, 256};
+    L.dn = TileShape{128, 512};
   }
   L.router = TileShape{T <= 2048 ? 16 : 64, 64};
   if (c.act_dtype == MOE_BF16 && T >= 4096) L.router = TileShape{128, 512};  // gemm_big.hip

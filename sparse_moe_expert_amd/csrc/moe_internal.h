@@ -102,10 +102,11 @@ struct GemmLaunch {
 
 hipError_t launch_gemm(int a_kind, int out_kind, TileShape ts, const GemmLaunch& g,
                        hipStream_t st);
-// Large-tile bf16 kernel (gemm_big.hip): 128 rows x 256 h-columns (gate/up)
-// or 128 rows x 512 output columns (projection).
+// Large-tile bf16 / fp8 kernel (gemm_big.hip): 128 rows x 256 h-columns
+// (gate/up) or 128 rows x 512 output columns (projection).
 bool gemm_big_supported(int a_kind, int out_kind, TileShape ts, bool dual);
-hipError_t launch_gemm_big(int out_kind, bool dual, const GemmLaunch& g, hipStream_t st);
+hipError_t launch_gemm_big(int a_kind, int out_kind, bool dual, const GemmLaunch& g,
+                           hipStream_t st);
 // Weight-streaming bf16 kernel (gemm_decode.hip): 16 or 32 rows x 64
 // h-columns (gate/up) or x 128 output columns (projection).
 bool gemm_decode_supported(int a_kind, int out_kind, TileShape ts, bool dual);
