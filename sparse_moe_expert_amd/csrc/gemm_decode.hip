@@ -12,11 +12,11 @@
 //    32 output columns, for 16*MT token rows, over the whole K.  A workgroup
 //    is 4 such waves side by side in N.
 //  * Weights go straight from HBM into registers, no LDS, no barriers: per
-//    128-wide K-block a lane loads 64 contiguous bytes of one weight row
-//    (4 x 16-byte loads), and the next K-block's loads are issued before the
-//    current block's MFMAs.  The MFMA K order is permuted accordingly (lane
-//    group g holds k in [32g, 32g+32) of the block, step s uses its s-th 8),
-//    identically for both operands, which leaves every dot product unchanged.
+//    128-wide K-block a lane makes 4 x 16-byte loads of one weight row, and
+//    the next K-block's loads are issued before the current block's MFMAs.
+//    Load s of lane group g (= lane / 16) reads chunk 4s + g of the block:
+//    one load instruction covers 64 contiguous bytes of each of 16 rows, and
+//    step s of the MFMA sees K in its natural order.
 //  * The expert's token rows (A) come from L2: all waves of the expert read
 //    the same few rows.
 //  * v_mfma_f32_16x16x32_bf16: rows = tokens (lane%16), columns = weight rows.
@@ -63,14 +63,14 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmLaunch p) {
     } else {
       wr = min(wn0 + t * 16 + lrow, N - 1);
     }
-    bptr[t] = job.W + wr * rowb_b + lgrp * 64;
+    bptr[t] = job.W + wr * rowb_b + lgrp * 16;
   }
   const char* aptr[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int r = min(m * 16 + lrow, job.rows_here - 1);
     const int src = gemm_a_source_row(p, job.row_begin + job.m0 + r);
-    aptr[m] = static_cast<const char*>(p.A) + src * rowb_a + lgrp * 64;
+    aptr[m] = static_cast<const char*>(p.A) + src * rowb_a + lgrp * 16;
   }
 
   auto load = [&](Regs<MT, NT>& R, int kb) {
@@ -78,11 +78,11 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmLaunch p) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) R.b[t][s] = *reinterpret_cast<const uint4*>(bptr[t] + off + s * 16);
+      for (int s = 0; s < 4; ++s) R.b[t][s] = *reinterpret_cast<const uint4*>(bptr[t] + off + s * 64);
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) R.a[m][s] = *reinterpret_cast<const uint4*>(aptr[m] + off + s * 16);
+      for (int s = 0; s < 4; ++s) R.a[m][s] = *reinterpret_cast<const uint4*>(aptr[m] + off + s * 64);
   };
 
   f32x4_t acc[MT][NT];
