@@ -165,7 +165,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
   const int rows_here = min(BM, rows - m0);
   const int n0 = nt * BN;
   const int K = p.K;
-  const int nk = K / Tr::KSTAGE;
+  // split K: this block's K-stages [kt_begin, kt_end), output at its own offset
+  int kt_begin = 0, kt_end = K / Tr::KSTAGE;
+  if (p.k_splits > 1) {
+    const int per = kt_end / p.k_splits;
+    kt_begin = blockIdx.y * per;
+    kt_end = kt_begin + per;
+    if constexpr (OK == K_F32) {
+      p.C = static_cast<float*>(p.C) + blockIdx.y * p.c_split_stride;
+      p.C2 = static_cast<float*>(p.C2) + blockIdx.y * p.c_split_stride;
+    }
+  }
   const long long row_bytes_a = p.lda * Tr::ESZ;
   const long long row_bytes_b = static_cast<long long>(K) * Tr::ESZ;
 
@@ -252,15 +262,15 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
     ws_up = WS + static_cast<long long>((p.N + n0) / kQBlock) * kblocks;
   }
 
-  gload(0);
+  gload(kt_begin);
   lstore(0);
   __syncthreads();
 
   const int lrow = lane & 15;
   const int lgrp = lane >> 4;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    const int cur = (kt - kt_begin) & 1;
+    if (kt + 1 < kt_end) gload(kt + 1);
     const char* As = smem + cur * C::STAGE;
     const char* Bs = As + C::A_BYTES;
     float bscale[C::NB];
@@ -313,7 +323,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
             }
           }
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
+    if (kt + 1 < kt_end) lstore(cur ^ 1);
     __syncthreads();
   }
 
@@ -411,8 +421,9 @@ hipError_t launch_t(const GemmLaunch& g, hipStream_t st) {
   if (total <= 0) return hipSuccess;
   const long long grid = ((total + 7) / 8) * 8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((grouped_gemm_kernel<AK, OK, BM, BN, DUAL>), dim3(static_cast<unsigned>(grid)),
-                     dim3(256), 0, st, g);
+  const unsigned splits = g.k_splits > 1 ? static_cast<unsigned>(g.k_splits) : 1u;
+  hipLaunchKernelGGL((grouped_gemm_kernel<AK, OK, BM, BN, DUAL>),
+                     dim3(static_cast<unsigned>(grid), splits), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 
@@ -433,9 +444,12 @@ hipError_t launch_shape(TileShape ts, const GemmLaunch& g, hipStream_t st) {
 hipError_t launch_gemm(int a_kind, int out_kind, TileShape ts, const GemmLaunch& g,
                        hipStream_t st) {
   const bool dual = g.dual != 0;
-  if (gemm_big_supported(a_kind, out_kind, ts, dual))
+  const bool split = g.k_splits > 1;  // only the generic kernel splits K
+  if (split && (out_kind != K_F32 || dual)) return hipErrorInvalidValue;
+  if (!split && gemm_big_supported(a_kind, out_kind, ts, dual))
     return launch_gemm_big(a_kind, out_kind, dual, g, st);
-  if (gemm_decode_supported(a_kind, out_kind, ts, dual)) return launch_gemm_decode(ts, dual, g, st);
+  if (!split && gemm_decode_supported(a_kind, out_kind, ts, dual))
+    return launch_gemm_decode(ts, dual, g, st);
   if (a_kind == K_F32 && out_kind == K_F32)
     return dual ? launch_shape<K_F32, K_F32, true>(ts, g, st)
                 : launch_shape<K_F32, K_F32, false>(ts, g, st);

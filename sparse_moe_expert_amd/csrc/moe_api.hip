@@ -117,14 +117,16 @@ hipError_t run_route(const moe_config_t& c, const Layout& L, const void* x, cons
   g.C2 = logits;
   g.c_split = LLONG_MAX;
   g.ldc = c.E;
+  g.k_splits = L.router_splits;
+  g.c_split_stride = static_cast<long long>(c.T) * c.E;
   hipError_t e = launch_gemm(act_kind(c), K_F32, L.router, g, st);
   if (e != hipSuccess) return e;
   if (ties) {
     e = launch_zero_i32(ties, 2, st);
     if (e != hipSuccess) return e;
   }
-  return launch_router_topk(logits, w.router_bias, c.T, c.E, c.k, c.norm_topk_prob,
-                            c.routed_scaling_factor, idx, tw, ties, st);
+  return launch_router_topk(logits, L.router_splits, w.router_bias, c.T, c.E, c.k,
+                            c.norm_topk_prob, c.routed_scaling_factor, idx, tw, ties, st);
 }
 
 hipError_t run_groups(const moe_config_t& c, const Layout& L, const int32_t* offsets,
@@ -288,7 +290,21 @@ Layout make_layout(const moe_config_t& c) {
     L.dn = TileShape{128, 512};
   }
   L.router = TileShape{T <= 2048 ? 16 : 64, 64};
-  if (c.act_dtype == MOE_BF16 && T >= 4096) L.router = TileShape{128, 512};  // gemm_big.hip
+  L.router_splits = 1;
+  if (c.act_dtype == MOE_BF16 && T >= 4096) {
+    L.router = TileShape{128, 512};  // gemm_big.hip
+  } else {
+    // Few output tiles (small T): split K so that the launch fills the chip.
+    // The partial sums are added in split order by the top-k kernel.
+    const size_t tiles = ((T + L.router.bm - 1) / L.router.bm) * ((E + L.router.bn - 1) / L.router.bn);
+    const int nk = static_cast<int>(H * asz / 128);  // 128-byte K-stages
+    for (int d = 8; d > 1; --d) {
+      if (nk % d == 0 && nk / d >= 4 && tiles * d <= 1024) {
+        L.router_splits = d;
+        break;
+      }
+    }
+  }
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -296,7 +312,7 @@ Layout make_layout(const moe_config_t& c) {
     off += align_up(bytes);
     return o;
   };
-  L.logits = take(T * E * 4);
+  L.logits = take(static_cast<size_t>(L.router_splits) * T * E * 4);
   L.topk_idx = take(T * k * 4);
   L.topk_w = take(T * k * 4);
   L.counts = take(E * 4);

@@ -44,7 +44,7 @@ struct TileShape {
 
 // Byte offsets of every buffer inside the caller's workspace.
 struct Layout {
-  size_t logits;        // [T, E] fp32
+  size_t logits;        // [router_splits, T, E] fp32 (split-K partial sums)
   size_t topk_idx;      // [T, k] int32
   size_t topk_w;        // [T, k] fp32
   size_t counts;        // [E] int32
@@ -63,6 +63,7 @@ struct Layout {
   size_t ysh;           // [S, T, H] fp32
   size_t total;
   int nchunks;
+  int router_splits;    // >= 1
   TileShape gu, dn, router;
 };
 
@@ -98,6 +99,10 @@ struct GemmLaunch {
   long long c_split;
   long long ldc;
   float* c_scale;          // FP8 output scales [rows, N/128]
+  // split K (generic kernel, fp32 output only): block y computes the K range
+  // [y * K / k_splits, (y + 1) * K / k_splits) into C + y * c_split_stride
+  int k_splits;            // 0 or 1: no split
+  long long c_split_stride;  // elements
 };
 
 hipError_t launch_gemm(int a_kind, int out_kind, TileShape ts, const GemmLaunch& g,
@@ -112,8 +117,9 @@ hipError_t launch_gemm_big(int a_kind, int out_kind, bool dual, const GemmLaunch
 bool gemm_decode_supported(int a_kind, int out_kind, TileShape ts, bool dual);
 hipError_t launch_gemm_decode(TileShape ts, bool dual, const GemmLaunch& g, hipStream_t st);
 
-hipError_t launch_router_topk(const float* logits, const float* bias, int T, int E, int k,
-                              int norm, float rsf, int32_t* idx, float* w, int32_t* ties,
+// logits: `splits` partial sums [splits][T][E] (added in split order).
+hipError_t launch_router_topk(const float* logits, int splits, const float* bias, int T, int E,
+                              int k, int norm, float rsf, int32_t* idx, float* w, int32_t* ties,
                               hipStream_t st);
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t st);
 

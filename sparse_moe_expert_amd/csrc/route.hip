@@ -25,6 +25,7 @@ constexpr int kPer = kMaxExperts / 64;
 __device__ __forceinline__ float sigmoidf_acc(float l) { return 1.0f / (1.0f + expf(-l)); }
 
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
+                                                          int splits,
                                                           const float* __restrict__ bias, int T,
                                                           int E, int k, int norm, float rsf,
                                                           int32_t* __restrict__ idx_out,
@@ -35,13 +36,17 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   if (t >= T) return;  // whole wave leaves together
 
   const float* lrow = logits + static_cast<long long>(t) * E;
+  const long long split_stride = static_cast<long long>(T) * E;
   float score[kPer];
   uint64_t key[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int e = i * 64 + lane;
     if (e < E) {
-      score[i] = sigmoidf_acc(lrow[e]);
+      // split-K partial sums, added in split order (deterministic)
+      float l = lrow[e];
+      for (int sp = 1; sp < splits; ++sp) l += lrow[sp * split_stride + e];
+      score[i] = sigmoidf_acc(l);
       const float c = score[i] + bias[e];
       key[i] = (static_cast<uint64_t>(f32_order_key(c)) << 32) | static_cast<uint32_t>(~e);
     } else {
@@ -114,14 +119,14 @@ __global__ void zero_i32_kernel(int32_t* p, int n) {
 
 }  // namespace
 
-hipError_t launch_router_topk(const float* logits, const float* bias, int T, int E, int k,
-                              int norm, float rsf, int32_t* idx, float* w, int32_t* ties,
+hipError_t launch_router_topk(const float* logits, int splits, const float* bias, int T, int E,
+                              int k, int norm, float rsf, int32_t* idx, float* w, int32_t* ties,
                               hipStream_t st) {
   if (T <= 0) return hipSuccess;
   const int waves_per_block = 4;
   const int grid = (T + waves_per_block - 1) / waves_per_block;
   hipLaunchKernelGGL(router_topk_kernel, dim3(grid), dim3(64 * waves_per_block), 0, st, logits,
-                     bias, T, E, k, norm, rsf, idx, w, ties);
+                     splits < 1 ? 1 : splits, bias, T, E, k, norm, rsf, idx, w, ties);
   return hipGetLastError();
 }
 
