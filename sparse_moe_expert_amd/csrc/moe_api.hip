@@ -276,8 +276,8 @@ Layout make_layout(const moe_config_t& c) {
   L.dn = TileShape{bm, bn};
   if (c.expert_dtype == MOE_BF16) {
     if (avg <= 12.0) {          // decode regime: weight streaming (gemm_decode.hip)
-      L.gu = TileShape{16, 64};
-      L.dn = TileShape{16, 128};
+      L.gu = TileShape{16, 128};
+      L.dn = TileShape{16, 256};
     } else if (avg <= 24.0) {
       L.gu = TileShape{32, 64};
       L.dn = TileShape{32, 128};
