@@ -10,6 +10,8 @@ config facts the pages print:
 * dots.llm1 lineage: top-6 of 128 routed + 2 shared, moe_intermediate 1408
   (Transformers "dots.llm1（Dots1）" article, model background list and the
   «MoE 路由与专家相关字段» table). The hidden size of that workload is 4096.
+* Router groups (n_group, topk_group; default 1 and 1) and rms_norm_eps 1e-6
+  come from the same article's field tables.
 
 This module holds shapes only; it computes nothing of the method.
 """
@@ -36,6 +38,9 @@ class MoEConfig:
     zipf_lambda: float = 0.10
     norm_topk_prob: bool = True
     routed_scaling_factor: float = 1.0
+    n_group: int = 1             # expert groups of the router (1: no grouping)
+    topk_group: int = 1          # groups a token may choose from
+    rms_norm_eps: float = 1e-6   # decoder-block RMSNorm epsilon
     weight_std: float = 0.02
     bias_half_width: float = 0.01
 

@@ -13,10 +13,11 @@ checkpoint itself cannot be pinned; the noaux_tc bias placement and the FP8
 scale convention are readings, pinned only for self-consistency.
 """
 from .moe_oracle import (E4M3_MAX, E4M3_TABLE, FP8_BLOCK, Dispatch, LayerResult, Routing,
-                         Weights, combine, decode_bf16, decode_e4m3, dense_layer_forward,
-                         dequantize_fp8_rows, dequantize_fp8_weight, dispatch, encode_e4m3,
-                         expert_forward, layer_forward, layer_inputs, quantize_fp8_rows, rms,
-                         route, route_inputs, sigmoid, sorted_expert_rows, swiglu_hidden,
-                         widen)
+                         Weights, block_forward, block_inputs, combine, decode_bf16,
+                         decode_e4m3, dense_layer_forward, dequantize_fp8_rows,
+                         dequantize_fp8_weight, dispatch, encode_bf16, encode_e4m3,
+                         expert_forward, group_scores, layer_forward, layer_inputs,
+                         quantize_fp8_rows, rms, rmsnorm, route, route_inputs, sigmoid,
+                         sorted_expert_rows, swiglu_hidden, widen)
 
 __all__ = [n for n in dir() if not n.startswith("_")]

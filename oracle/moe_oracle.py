@@ -27,7 +27,20 @@ design notes of the repository):
 * Scores are sigmoid of the router logits [AA «稀疏激活»]; the softmax in the
   [DD §3.1] snippet is overruled by the config-level statement.
 * noaux_tc: a per-expert bias is added to the sigmoid score to choose the
-  experts; the weights use the unbiased scores.  No expert grouping.
+  experts; the weights use the unbiased scores.
+* Group-limited routing [D1 «MoE 路由与专家相关字段»: n_group experts groups,
+  topk_group groups chosen by a group score, then the top-k inside them; the
+  article maps the fields to DeepSeek-V3's router].  The group score is not
+  defined on the pages; reading: the sum of the two largest selection keys
+  (score + bias) of the group (the whole group if it has one expert), groups
+  ordered by score descending, lower group index first.  n_group = 1 is the
+  plain top-k.
+* Decoder block around the layer [DD §3.3 figure: "Residual + RMSNorm", MoE
+  FFN, "Residual + Output"; D1: RMSNorm computes the variance in fp32, then
+  rsqrt, then multiplies the weight; rms_norm_eps 1e-6]:
+  out = h + MoE(RMSNorm(h)), RMSNorm(h) = gamma * h / sqrt(mean(h^2) + eps),
+  with the normalised activations stored in the activation type (they are the
+  layer's input tensor).
 * Top-k order: key descending, lower expert index first among equal keys.
 * Expert FFN = SwiGLU without biases: h = SiLU(x Wg^T) * (x Wu^T), y = h Wd^T,
   gate rows first in the packed gate_up weight [D1 «并行策略字段»].
@@ -153,26 +166,50 @@ class Routing:
     w: np.ndarray          # [T, k]  routing weights
     gap_sel: np.ndarray    # [T]     c_(k-1) - c_(k)  (0-based sorted positions)
     gap_ord: np.ndarray    # [T]     min_j<k-1 c_(j) - c_(j+1)
+    gap_grp: np.ndarray = None  # [T] group score gap at the topk_group boundary
+
+
+def group_scores(c: np.ndarray, n_group: int) -> np.ndarray:
+    """[T, n_group]: per group of E / n_group consecutive experts, the sum of
+    its two largest selection keys (its only key if the group has one)."""
+    T, E = c.shape
+    G = E // n_group
+    top = np.sort(c.reshape(T, n_group, G), axis=2)[:, :, ::-1]
+    return top[:, :, :min(2, G)].sum(axis=2)
 
 
 def route(x: np.ndarray, w_router: np.ndarray, bias: np.ndarray, k: int,
-          norm_topk_prob: bool = True, routed_scaling_factor: float = 1.0) -> Routing:
+          norm_topk_prob: bool = True, routed_scaling_factor: float = 1.0,
+          n_group: int = 1, topk_group: int = 1) -> Routing:
     """Gate = Linear(hidden -> E, no bias) [DD §3.1, §3.3 "Gate (Linear 5120→256)"];
-    sigmoid scores and noaux_tc selection [AA «稀疏激活»]; top-k then
-    renormalisation over the k chosen scores [DD §3.1; AA norm_topk_prob];
-    routed_scaling_factor [D1 MoE fields]."""
+    sigmoid scores and noaux_tc selection [AA «稀疏激活»]; optional group
+    limit [D1 n_group / topk_group]; top-k then renormalisation over the k
+    chosen scores [DD §3.1; AA norm_topk_prob]; routed_scaling_factor
+    [D1 MoE fields]."""
     x = np.asarray(x, dtype=np.float64)
     w_router = np.asarray(w_router, dtype=np.float64)
     T = x.shape[0]
     E = w_router.shape[0]
     assert 1 <= k <= E
+    assert n_group >= 1 and E % n_group == 0 and 1 <= topk_group <= n_group
+    assert k <= topk_group * (E // n_group)
     logits = x @ w_router.T
     s = sigmoid(logits)
     c = s + np.asarray(bias, dtype=np.float64)[None, :]
+    # group limit: keep the experts of the topk_group best groups
+    gs = group_scores(c, n_group)
+    g_order = np.argsort(-gs, axis=1, kind="stable")
+    gss = np.take_along_axis(gs, g_order, axis=1)
+    gap_grp = (gss[:, topk_group - 1] - gss[:, topk_group] if topk_group < n_group
+               else np.full(T, np.inf))
+    keep = np.zeros((T, n_group), bool)
+    np.put_along_axis(keep, g_order[:, :topk_group], True, axis=1)
+    allowed = np.repeat(keep, E // n_group, axis=1)
+    cm = np.where(allowed, c, -np.inf)
     # stable sort of -c: descending key, equal keys keep ascending expert index
-    order = np.argsort(-c, axis=1, kind="stable")
+    order = np.argsort(-cm, axis=1, kind="stable")
     idx = order[:, :k].astype(np.int32)
-    cs = np.take_along_axis(c, order, axis=1)
+    cs = np.take_along_axis(cm, order, axis=1)
     gap_sel = cs[:, k - 1] - cs[:, k] if k < E else np.full(T, np.inf)
     if k >= 2:
         gap_ord = np.min(cs[:, :k - 1] - cs[:, 1:k], axis=1)
@@ -184,7 +221,7 @@ def route(x: np.ndarray, w_router: np.ndarray, bias: np.ndarray, k: int,
     else:
         w = chosen.copy()
     w = w * routed_scaling_factor
-    return Routing(logits, s, c, idx, w, gap_sel, gap_ord)
+    return Routing(logits, s, c, idx, w, gap_sel, gap_ord, gap_grp)
 
 
 # --------------------------------------------------------------------------
@@ -295,7 +332,7 @@ def layer_inputs(cfg, inp: dict, tokens=None):
 def route_inputs(cfg, inp: dict, tokens=None) -> Routing:
     x_r, _ = layer_inputs(cfg, inp, tokens)
     return route(x_r, widen(inp["w_router"], cfg.act), inp["bias"], cfg.k,
-                 cfg.norm_topk_prob, cfg.routed_scaling_factor)
+                 cfg.norm_topk_prob, cfg.routed_scaling_factor, cfg.n_group, cfg.topk_group)
 
 
 @dataclass
@@ -315,7 +352,7 @@ def layer_forward(cfg, inp: dict, tokens=None) -> LayerResult:
     tokens = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
     x_r, x_e = layer_inputs(cfg, inp, tokens)
     r = route(x_r, widen(inp["w_router"], cfg.act), inp["bias"], cfg.k,
-              cfg.norm_topk_prob, cfg.routed_scaling_factor)
+              cfg.norm_topk_prob, cfg.routed_scaling_factor, cfg.n_group, cfg.topk_group)
     n, H, k = tokens.size, cfg.H, cfg.k
     W = Weights(cfg, inp)
     y = np.zeros((n, k, H))
@@ -334,7 +371,7 @@ def dense_layer_forward(cfg, inp: dict) -> np.ndarray:
     routing mask m[t,e] = w[t,j] if idx[t,j] = e, else 0.  No dispatch."""
     x_r, x_e = layer_inputs(cfg, inp)
     r = route(x_r, widen(inp["w_router"], cfg.act), inp["bias"], cfg.k,
-              cfg.norm_topk_prob, cfg.routed_scaling_factor)
+              cfg.norm_topk_prob, cfg.routed_scaling_factor, cfg.n_group, cfg.topk_group)
     W = Weights(cfg, inp)
     m = np.zeros((cfg.T, cfg.E))
     for j in range(cfg.k):
@@ -395,6 +432,58 @@ def combine(y_sorted: np.ndarray, y_shared: np.ndarray, w: np.ndarray,
     for j in range(k):
         out = out + w[:, j:j + 1] * np.asarray(y_sorted, np.float64)[inv[np.arange(T) * k + j]]
     return out
+
+
+# --------------------------------------------------------------------------
+# Decoder block around the layer: RMSNorm before, residual add after
+# --------------------------------------------------------------------------
+
+def rmsnorm(h: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """gamma * h / sqrt(mean(h^2) + eps) per row [D1: variance, rsqrt, times
+    the weight; DD §3.3 "Residual + RMSNorm"]."""
+    h = np.asarray(h, dtype=np.float64)
+    ms = np.mean(h * h, axis=-1, keepdims=True)
+    return np.asarray(gamma, dtype=np.float64)[None, :] * (h / np.sqrt(ms + eps))
+
+
+def encode_bf16(v: np.ndarray) -> np.ndarray:
+    """fp64 -> bf16 bit patterns with round-to-nearest-even, decided on the
+    fp64 value itself (no double rounding through fp32).  Finite inputs."""
+    v = np.asarray(v, dtype=np.float64)
+    bits = v.astype(np.float32).view(np.uint32)
+    hi = (bits >> 16).astype(np.uint32)          # bf16 truncation of the fp32 value
+    lo_val = (hi << 16).view(np.float32).astype(np.float64)          # |lo_val| <= |v|, or equal up to fp32 rounding
+    hi_val = ((hi + 1) << 16).view(np.float32).astype(np.float64)    # next bf16 away from zero
+    a, lo_a, hi_a = np.abs(v), np.abs(lo_val), np.abs(hi_val)
+    mid = (lo_a + hi_a) / 2.0                    # exact in fp64
+    up = (a > mid) | ((a == mid) & ((hi & 1) == 1))
+    return np.where(up, hi + 1, hi).astype(np.uint16)
+
+
+def block_inputs(cfg, inp: dict, gamma: np.ndarray, tokens=None):
+    """(h, xn_storage): the residual input h (fp64) and the normalised layer
+    input in storage format (the activation type)."""
+    h_st = inp["x"] if tokens is None else inp["x"][tokens]
+    h = widen(h_st, cfg.act)
+    xn = rmsnorm(h, gamma, cfg.rms_norm_eps)
+    if cfg.act == "bf16":
+        xn_st = encode_bf16(xn)
+    else:
+        xn_st = xn.astype(np.float32)
+    return h, xn_st
+
+
+def block_forward(cfg, inp: dict, gamma: np.ndarray, tokens=None):
+    """out = h + MoE(RMSNorm(h)) [DD §3.3 figure: "Residual + RMSNorm", MoE
+    FFN, "Residual + Output"].  Returns (out fp64 [n, H], LayerResult)."""
+    tokens = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
+    h, xn_st = block_inputs(cfg, inp, gamma, tokens)
+    # the layer on the normalised rows only (x replaced by the normalised subset)
+    full = dict(inp)
+    full["x"] = np.zeros_like(inp["x"])
+    full["x"][tokens] = xn_st
+    res = layer_forward(cfg, full, tokens)
+    return h + res.out, res
 
 
 def rms(a: np.ndarray) -> float:

@@ -22,7 +22,7 @@ def _golden_layer():
     d = g["dims"]
     cfg = SimpleNamespace(T=d["T"], H=d["H"], E=d["E"], S=d["S"], k=d["k"], I=d["I"],
                           Is=d["Is"], act="f64", expert="f64", norm_topk_prob=True,
-                          routed_scaling_factor=1.0)
+                          routed_scaling_factor=1.0, n_group=1, topk_group=1)
     wg = np.array(g["w_gate_in_units_of_ln3"]) * L3
     wu = np.array(g["w_up"], float)
     inp = {
