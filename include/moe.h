@@ -17,8 +17,10 @@
  *       hidden 5120, moe_intermediate 1536, BF16/FP8).
  *  [D1] "Transformers 中的 dots.llm1（Dots1）模型" -- «MoE 路由与专家相关字段»
  *       table (n_routed_experts, num_experts_per_tok, n_shared_experts,
- *       norm_topk_prob, routed_scaling_factor, moe_intermediate_size) and
- *       «并行策略字段» (packed gate_up_proj, down_proj, grouped_gemm).
+ *       n_group, topk_group, norm_topk_prob, routed_scaling_factor,
+ *       moe_intermediate_size), «并行策略字段» (packed gate_up_proj,
+ *       down_proj, grouped_gemm), and the RMSNorm description (fp32
+ *       variance, rsqrt, times the weight; rms_norm_eps 1e-6).
  *
  * Conventions for every entry point:
  *  - All tensor arguments are DEVICE pointers owned by the caller, row-major,
@@ -75,6 +77,11 @@ typedef struct moe_config {
   int32_t act_dtype;    /* x, router weight and output: MOE_F32 | MOE_BF16  */
   int32_t expert_dtype; /* expert weights: MOE_F32 (act F32), MOE_BF16 or
                            MOE_FP8_E4M3 (act BF16)                          */
+  int32_t n_group;      /* router expert groups; 0 or 1: no grouping.  E must
+                           be a multiple, with at most 64 groups [D1]       */
+  int32_t topk_group;   /* groups a token may choose from, 1..n_group
+                           (ignored without grouping); k <= topk_group *
+                           E / n_group                                       */
 } moe_config_t;
 
 /* Weights of one layer (device pointers).
@@ -123,16 +130,21 @@ size_t moe_workspace_size(const moe_config_t* cfg);
 /* Router [DD §3.1 steps 1-2; AA «稀疏激活»]: for every token t
  *   l[t,e] = Σ_h x[t,h] * w_router[e,h]      (fp32 accumulate, never bf16)
  *   s = 1 / (1 + exp(-l));   c = s + router_bias   (c used for the choice only)
+ *   with n_group > 1 [D1 n_group / topk_group]: the experts form n_group
+ *       groups of E / n_group consecutive indices; a group's score is the
+ *       sum of its two largest c (its only c if it has one expert); only the
+ *       experts of the topk_group groups of largest score (lower group index
+ *       first among equal scores) take part in the choice below
  *   topk_idx[t, 0..k) = the k experts of largest c, in decreasing c, the lower
  *                       expert index first among equal c
  *   topk_w[t, j] = s[t, idx_j] / Σ_j' s[t, idx_j'] * routed_scaling_factor
  *                  (without the division when norm_topk_prob == 0)
  * x [T, H] act_dtype; topk_idx [T, k] int32; topk_w [T, k] fp32.
  * tie_counts: NULL, or int32[2] that receives the number of tokens whose
- * k-th and (k+1)-th keys (index 0), resp. some two consecutive chosen keys
- * (index 1), differ by <= 1e-6 in fp32 -- tokens where another choice or slot
- * order is equally valid at fp32 precision.  Workspace: holds the fp32
- * logits [T, E]. */
+ * k-th and (k+1)-th keys, or topk_group-th and next group scores (index 0),
+ * resp. some two consecutive chosen keys (index 1), differ by <= 1e-6 in
+ * fp32 -- tokens where another choice or slot order is equally valid at
+ * fp32 precision.  Workspace: holds the fp32 logits. */
 moe_status_t moe_route(const moe_config_t* cfg, const void* x, const moe_weights_t* w,
                        int32_t* topk_idx, float* topk_w, int32_t* tie_counts,
                        void* workspace, size_t workspace_bytes, moe_stream_t stream);
@@ -205,6 +217,29 @@ moe_status_t moe_quantize_fp8(const void* x_bf16, int32_t rows, int32_t cols, ui
 moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
                                void* out, int32_t* opt_counts, int32_t* opt_tie_counts,
                                void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* RMSNorm of the decoder block [DD §3.3 figure "Residual + RMSNorm"; D1:
+ * variance in fp32, rsqrt, times the weight]: for every row t of h [T, H]
+ *   out[t, c] = gamma[c] * h[t, c] / sqrt(mean_c' h[t, c']^2 + eps)
+ * computed in fp32 (sum of squares in a fixed order) with one rounding to
+ * act_dtype.  h, gamma [H] and out are act_dtype; out may not alias h.
+ * eps must be finite and >= 0. */
+moe_status_t moe_rmsnorm(const moe_config_t* cfg, const void* h, const void* gamma, float eps,
+                         void* out, moe_stream_t stream);
+
+/* The MoE half of a decoder block [DD §3.3 figure: "Residual + RMSNorm", MoE
+ * FFN layer, "Residual + Output"]:
+ *   x = moe_rmsnorm(h)           (stored in act_dtype, the layer's input)
+ *   out[t] = h[t] + moe_layer_forward(x)[t]
+ * with the residual added inside the combine: h + shared + Σ_j w_j y_j is
+ * accumulated in fp32 in that order and rounded to act_dtype once.
+ * h, out [T, H] act_dtype (out may not alias h); gamma [H] act_dtype.
+ * opt_counts, opt_tie_counts and the workspace as for moe_layer_forward;
+ * the workspace also holds x (moe_workspace_size covers it). */
+moe_status_t moe_block_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* h,
+                               const void* gamma, float eps, void* out, int32_t* opt_counts,
+                               int32_t* opt_tie_counts, void* workspace, size_t workspace_bytes,
+                               moe_stream_t stream);
 
 /* moe_layer_forward that also records HIP events on `stream` at its stage
  * boundaries, for timing each stage on the stream it runs on:

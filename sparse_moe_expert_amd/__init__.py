@@ -1,7 +1,8 @@
-"""MI355X (gfx950) MoE layer forward: sigmoid/noaux_tc router, stable
-dispatch, grouped SwiGLU expert GEMMs (bf16 / fp8 e4m3 MFMA), shared expert
-and deterministic combine, as hand-written HIP kernels behind the C ABI of
-include/moe.h (libmoe.so).
+"""MI355X (gfx950) MoE layer forward: sigmoid/noaux_tc router (optionally
+group-limited), stable dispatch, grouped SwiGLU expert GEMMs (bf16 / fp8 e4m3
+MFMA), shared expert and deterministic combine, plus the decoder block around
+it (RMSNorm before, residual after), as hand-written HIP kernels behind the C
+ABI of include/moe.h (libmoe.so).
 
 This package is the ctypes binding (``_lib``) plus device-buffer plumbing
 (``device``).  The binding loads on first use of any of its names and raises
@@ -15,7 +16,7 @@ _BINDING = (
     "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_F32", "MOE_FP8_E4M3", "MOE_OK", "MoEError",
     "make_config", "make_weights", "moe_combine", "moe_config_t", "moe_dispatch",
     "moe_expert_down", "moe_expert_gate_up", "moe_grouped_ffn", "moe_layer_forward",
-    "moe_layer_forward_timed",
+    "moe_layer_forward_timed", "moe_rmsnorm", "moe_block_forward",
     "moe_quantize_fp8", "moe_route", "moe_weights_t", "moe_workspace_size", "status_string",
     "version", "last_error_detail",
 )

@@ -20,7 +20,8 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 # every entry point of include/moe.h
 EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_version", "moe_workspace_size", "moe_route",
            "moe_dispatch", "moe_grouped_ffn", "moe_expert_gate_up", "moe_expert_down",
-           "moe_combine", "moe_quantize_fp8", "moe_layer_forward", "moe_layer_forward_timed")
+           "moe_combine", "moe_quantize_fp8", "moe_layer_forward", "moe_layer_forward_timed",
+           "moe_rmsnorm", "moe_block_forward")
 
 
 class MoEError(RuntimeError):
@@ -36,7 +37,8 @@ class moe_config_t(ctypes.Structure):
                 ("S", ctypes.c_int32), ("k", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("I_shared", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
                 ("routed_scaling_factor", ctypes.c_float), ("act_dtype", ctypes.c_int32),
-                ("expert_dtype", ctypes.c_int32)]
+                ("expert_dtype", ctypes.c_int32), ("n_group", ctypes.c_int32),
+                ("topk_group", ctypes.c_int32)]
 
 
 class moe_weights_t(ctypes.Structure):
@@ -73,6 +75,9 @@ def _load():
         "moe_layer_forward": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P, SZ, P]),
         "moe_layer_forward_timed": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P, SZ, P,
                                                    ctypes.POINTER(ctypes.c_void_p)]),
+        "moe_rmsnorm": (ctypes.c_int, [CP, P, P, ctypes.c_float, P, P]),
+        "moe_block_forward": (ctypes.c_int, [CP, WP, P, P, ctypes.c_float, P, I32P, I32P, P, SZ,
+                                             P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -97,10 +102,11 @@ def version() -> str:
 
 
 def make_config(T, H, E, S, k, I, I_shared=None, act="bf16", expert="bf16",
-                norm_topk_prob=True, routed_scaling_factor=1.0) -> moe_config_t:
+                norm_topk_prob=True, routed_scaling_factor=1.0, n_group=1,
+                topk_group=1) -> moe_config_t:
     return moe_config_t(T, H, E, S, k, I, I if I_shared is None else I_shared,
                         1 if norm_topk_prob else 0, float(routed_scaling_factor),
-                        DTYPES[act], DTYPES[expert])
+                        DTYPES[act], DTYPES[expert], int(n_group), int(topk_group))
 
 
 def _ptr(t) -> int | None:
@@ -203,3 +209,16 @@ def moe_layer_forward_timed(cfg, weights, x, out, events, opt_counts=None, opt_t
     _check(LIB.moe_layer_forward_timed(ctypes.byref(cfg), ctypes.byref(weights), _ptr(x),
                                        _ptr(out), _ptr(opt_counts), _ptr(opt_tie_counts), wp, wb,
                                        _stream(stream), arr), "moe_layer_forward_timed")
+
+
+def moe_rmsnorm(cfg, h, gamma, eps, out, stream=None):
+    _check(LIB.moe_rmsnorm(ctypes.byref(cfg), _ptr(h), _ptr(gamma), float(eps), _ptr(out),
+                           _stream(stream)), "moe_rmsnorm")
+
+
+def moe_block_forward(cfg, weights, h, gamma, eps, out, opt_counts=None, opt_tie_counts=None,
+                      workspace=None, stream=None):
+    wp, wb = _ws(workspace)
+    _check(LIB.moe_block_forward(ctypes.byref(cfg), ctypes.byref(weights), _ptr(h), _ptr(gamma),
+                                 float(eps), _ptr(out), _ptr(opt_counts), _ptr(opt_tie_counts),
+                                 wp, wb, _stream(stream)), "moe_block_forward")

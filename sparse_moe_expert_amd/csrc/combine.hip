@@ -5,7 +5,8 @@
 // (Deep Dive §3.1 forward; §3.3 figure "Weighted sum" then "Shared Expert
 // (always) … add").  One workgroup per token gathers its k fp32 rows in slot
 // order; fp32 accumulation in a fixed order, one rounding to the output type
-// at the store, no atomics.
+// at the store, no atomics.  In a block forward the residual stream is added
+// first (§3.3 figure, "Residual + Output").
 //
 // Quantisation: per row and 128 channels, scale = amax / 448 (fp32, 1 for an
 // all-zero block) and code = e4m3(v / scale), round to nearest even -- the
@@ -22,6 +23,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const float* __restrict__ ysh,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ inv,
+                                                      const void* __restrict__ residual,
                                                       void* __restrict__ out, int T, int H, int k,
                                                       int S) {
   __shared__ float ws[kMaxTopK];
@@ -34,6 +36,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   __syncthreads();
   for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
     float4 acc = float4{0.f, 0.f, 0.f, 0.f};
+    if (residual) {
+      // decoder block: the residual stream comes first
+      if constexpr (OK == K_BF16) {
+        const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(residual) +
+                                                        static_cast<long long>(t) * H + c);
+        acc = float4{bf16_to_f32(static_cast<uint16_t>(r.x & 0xFFFF)),
+                     bf16_to_f32(static_cast<uint16_t>(r.x >> 16)),
+                     bf16_to_f32(static_cast<uint16_t>(r.y & 0xFFFF)),
+                     bf16_to_f32(static_cast<uint16_t>(r.y >> 16))};
+      } else {
+        acc = *reinterpret_cast<const float4*>(static_cast<const float*>(residual) +
+                                               static_cast<long long>(t) * H + c);
+      }
+    }
     for (int s = 0; s < S; ++s) {
       const float4 v = *reinterpret_cast<const float4*>(ysh + (static_cast<long long>(s) * T + t) * H + c);
       acc.x += v.x;
@@ -98,17 +114,17 @@ __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t* __r
 }  // namespace
 
 hipError_t launch_combine(int act_kind, const void* y, const void* ysh, const float* w,
-                          const int32_t* inv, void* out, int T, int H, int k, int S,
-                          hipStream_t st) {
+                          const int32_t* inv, const void* residual, void* out, int T, int H, int k,
+                          int S, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   const float* yf = static_cast<const float*>(y);
   const float* yshf = static_cast<const float*>(ysh);
   if (act_kind == K_BF16)
-    hipLaunchKernelGGL(combine_kernel<K_BF16>, dim3(T), dim3(256), 0, st, yf, yshf, w, inv, out,
-                       T, H, k, S);
+    hipLaunchKernelGGL(combine_kernel<K_BF16>, dim3(T), dim3(256), 0, st, yf, yshf, w, inv,
+                       residual, out, T, H, k, S);
   else
-    hipLaunchKernelGGL(combine_kernel<K_F32>, dim3(T), dim3(256), 0, st, yf, yshf, w, inv, out,
-                       T, H, k, S);
+    hipLaunchKernelGGL(combine_kernel<K_F32>, dim3(T), dim3(256), 0, st, yf, yshf, w, inv,
+                       residual, out, T, H, k, S);
   return hipGetLastError();
 }
 

@@ -34,6 +34,14 @@ moe_status_t check_config(const moe_config_t* c) {
   if (c->E > kMaxExperts || c->S > kMaxShared || c->k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
   if (c->H % kQBlock != 0 || c->I % kQBlock != 0) return MOE_ERR_UNSUPPORTED;
   if (c->I_shared != c->I) return MOE_ERR_UNSUPPORTED;
+  // group-limited routing: n_group 0 or 1 means none
+  if (c->n_group < 0) return MOE_ERR_INVALID_ARG;
+  if (c->n_group > 1) {
+    if (c->E % c->n_group != 0 || c->topk_group < 1 || c->topk_group > c->n_group)
+      return MOE_ERR_INVALID_ARG;
+    if (c->k > c->topk_group * (c->E / c->n_group)) return MOE_ERR_INVALID_ARG;
+    if (c->n_group > 64) return MOE_ERR_UNSUPPORTED;
+  }
   // expert storage must match the activation type (FP8 experts take bf16 x)
   if (c->act_dtype == MOE_F32 && c->expert_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
   if (c->act_dtype == MOE_BF16 && c->expert_dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
@@ -126,7 +134,8 @@ hipError_t run_route(const moe_config_t& c, const Layout& L, const void* x, cons
     if (e != hipSuccess) return e;
   }
   return launch_router_topk(logits, L.router_splits, w.router_bias, c.T, c.E, c.k,
-                            c.norm_topk_prob, c.routed_scaling_factor, idx, tw, ties, st);
+                            c.n_group > 1 ? c.n_group : 1, c.topk_group, c.norm_topk_prob,
+                            c.routed_scaling_factor, idx, tw, ties, st);
 }
 
 hipError_t run_groups(const moe_config_t& c, const Layout& L, const int32_t* offsets,
@@ -185,10 +194,9 @@ hipError_t record(void* const* events, int i, hipStream_t st) {
   return hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
 }
 
-// The whole layer; `events` (7 or null) are recorded at the stage boundaries.
-moe_status_t layer_impl(const moe_config_t* cfg, const moe_weights_t* w, const void* x, void* out,
-                        int32_t* opt_counts, int32_t* opt_tie_counts, void* workspace,
-                        size_t workspace_bytes, moe_stream_t stream, void* const* events) {
+moe_status_t check_layer_args(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                              void* out, void* workspace, size_t workspace_bytes,
+                              void* const* events) {
   moe_status_t s = check_config(cfg);
   if (s != MOE_OK) return s;
   if ((s = check_weights(*cfg, w, true, true)) != MOE_OK) return s;
@@ -198,9 +206,17 @@ moe_status_t layer_impl(const moe_config_t* cfg, const moe_weights_t* w, const v
   if (events)
     for (int i = 0; i < 7; ++i)
       if (!events[i]) return MOE_ERR_INVALID_ARG;
-  const moe_config_t& c = *cfg;
+  return MOE_OK;
+}
+
+// The whole layer, arguments already checked; `events` (7 or null) are
+// recorded at the stage boundaries; `residual` (null or [T, H]) is added in
+// the combine.
+hipError_t layer_run(const moe_config_t& c, const moe_weights_t* w, const void* x,
+                     const void* residual, void* out, int32_t* opt_counts,
+                     int32_t* opt_tie_counts, void* workspace, hipStream_t st,
+                     void* const* events) {
   const Layout L = make_layout(c);
-  hipStream_t st = static_cast<hipStream_t>(stream);
   void* ws = workspace;
   int32_t* idx = at<int32_t>(ws, L.topk_idx);
   float* tw = at<float>(ws, L.topk_w);
@@ -211,7 +227,6 @@ moe_status_t layer_impl(const moe_config_t* cfg, const moe_weights_t* w, const v
   void* y = at<char>(ws, L.y);
   void* ysh = at<char>(ws, L.ysh);
 
-  clear_stale_error();
   hipError_t e = record(events, 0, st);
   if (e == hipSuccess) e = run_route(c, L, x, *w, idx, tw, opt_tie_counts, ws, st);
   if (e == hipSuccess) e = record(events, 1, st);
@@ -228,9 +243,20 @@ moe_status_t layer_impl(const moe_config_t* cfg, const moe_weights_t* w, const v
   if (e == hipSuccess) e = record(events, 4, st);
   if (e == hipSuccess) e = run_down(c, L, y, ysh, ws, st);
   if (e == hipSuccess) e = record(events, 5, st);
-  if (e == hipSuccess) e = launch_combine(act_kind(c), y, ysh, tw, inv, out, c.T, c.H, c.k, c.S, st);
+  if (e == hipSuccess)
+    e = launch_combine(act_kind(c), y, ysh, tw, inv, residual, out, c.T, c.H, c.k, c.S, st);
   if (e == hipSuccess) e = record(events, 6, st);
-  return hip_status(e);
+  return e;
+}
+
+moe_status_t layer_impl(const moe_config_t* cfg, const moe_weights_t* w, const void* x, void* out,
+                        int32_t* opt_counts, int32_t* opt_tie_counts, void* workspace,
+                        size_t workspace_bytes, moe_stream_t stream, void* const* events) {
+  moe_status_t s = check_layer_args(cfg, w, x, out, workspace, workspace_bytes, events);
+  if (s != MOE_OK || cfg->T == 0) return s;
+  clear_stale_error();
+  return hip_status(layer_run(*cfg, w, x, nullptr, out, opt_counts, opt_tie_counts, workspace,
+                              static_cast<hipStream_t>(stream), events));
 }
 
 hipError_t run_down(const moe_config_t& c, const Layout& L, void* y_sorted, void* y_shared,
@@ -329,6 +355,7 @@ Layout make_layout(const moe_config_t& c) {
   L.hs = take(fp8 ? rows_all * (I / kQBlock) * 4 : 0);
   L.y = take(R * H * 4);        // fp32: rounded once, in the combine
   L.ysh = take(S * T * H * 4);
+  L.xn = take(T * H * asz);
   L.total = off;
   return L;
 }
@@ -457,8 +484,8 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y_sorted, const vo
   if (cfg->S > 0 && (!y_shared || !aligned16(y_shared))) return MOE_ERR_INVALID_ARG;
   const moe_config_t& c = *cfg;
   clear_stale_error();
-  return hip_status(launch_combine(act_kind(c), y_sorted, y_shared, topk_w, inv, out, c.T, c.H,
-                                   c.k, c.S, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_combine(act_kind(c), y_sorted, y_shared, topk_w, inv, nullptr, out,
+                                   c.T, c.H, c.k, c.S, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_quantize_fp8(const void* x_bf16, int32_t rows, int32_t cols, uint8_t* q,
@@ -486,6 +513,39 @@ moe_status_t moe_layer_forward_timed(const moe_config_t* cfg, const moe_weights_
   if (!events) return MOE_ERR_INVALID_ARG;
   return layer_impl(cfg, w, x, out, opt_counts, opt_tie_counts, workspace, workspace_bytes, stream,
                     events);
+}
+
+moe_status_t moe_rmsnorm(const moe_config_t* cfg, const void* h, const void* gamma, float eps,
+                         void* out, moe_stream_t stream) {
+  moe_status_t s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!std::isfinite(eps) || eps < 0.f) return MOE_ERR_INVALID_ARG;
+  if (cfg->T == 0) return MOE_OK;
+  if (!h || !aligned16(h) || !gamma || !aligned16(gamma) || !out || !aligned16(out) || out == h)
+    return MOE_ERR_INVALID_ARG;
+  clear_stale_error();
+  return hip_status(launch_rmsnorm(act_kind(*cfg), h, gamma, eps, out, cfg->T, cfg->H,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_block_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* h,
+                               const void* gamma, float eps, void* out, int32_t* opt_counts,
+                               int32_t* opt_tie_counts, void* workspace, size_t workspace_bytes,
+                               moe_stream_t stream) {
+  moe_status_t s = check_layer_args(cfg, w, h, out, workspace, workspace_bytes, nullptr);
+  if (s != MOE_OK) return s;
+  if (!std::isfinite(eps) || eps < 0.f) return MOE_ERR_INVALID_ARG;
+  if (cfg->T == 0) return MOE_OK;
+  if (!gamma || !aligned16(gamma) || out == h) return MOE_ERR_INVALID_ARG;
+  const moe_config_t& c = *cfg;
+  const Layout L = make_layout(c);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* xn = at<char>(workspace, L.xn);
+  clear_stale_error();
+  hipError_t e = launch_rmsnorm(act_kind(c), h, gamma, eps, xn, c.T, c.H, st);
+  if (e == hipSuccess)
+    e = layer_run(c, w, xn, h, out, opt_counts, opt_tie_counts, workspace, st, nullptr);
+  return hip_status(e);
 }
 
 }  // extern "C"

@@ -61,6 +61,7 @@ struct Layout {
   size_t hs;            // FP8: [R + S*T, I/128] fp32 scales
   size_t y;             // [R, H] fp32  (routed expert outputs, sorted)
   size_t ysh;           // [S, T, H] fp32
+  size_t xn;            // [T, H] act type: the normalised input of a block forward
   size_t total;
   int nchunks;
   int router_splits;    // >= 1
@@ -119,8 +120,11 @@ hipError_t launch_gemm_decode(TileShape ts, bool dual, const GemmLaunch& g, hipS
 
 // logits: `splits` partial sums [splits][T][E] (added in split order).
 hipError_t launch_router_topk(const float* logits, int splits, const float* bias, int T, int E,
-                              int k, int norm, float rsf, int32_t* idx, float* w, int32_t* ties,
-                              hipStream_t st);
+                              int k, int n_group, int topk_group, int norm, float rsf, int32_t* idx,
+                              float* w, int32_t* ties, hipStream_t st);
+// RMSNorm rows of [T, H] (act kind F32 or BF16), fp32 math, one rounding.
+hipError_t launch_rmsnorm(int act_kind, const void* h, const void* gamma, float eps, void* out,
+                          int T, int H, hipStream_t st);
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t st);
 
 hipError_t launch_dispatch(const int32_t* topk_idx, int T, int k, int E, int S,
@@ -142,8 +146,9 @@ hipError_t launch_groups_only(const int32_t* offsets, int T, int k, int E, int S
 hipError_t launch_quant_rows_fp8(const uint16_t* x_bf16, int rows, int cols, uint8_t* q,
                                  float* scales, hipStream_t st);
 
+// residual: null, or [T, H] of the act kind, added first (block forward)
 hipError_t launch_combine(int act_kind, const void* y, const void* ysh, const float* w,
-                          const int32_t* inv, void* out, int T, int H, int k, int S,
-                          hipStream_t st);
+                          const int32_t* inv, const void* residual, void* out, int T, int H, int k,
+                          int S, hipStream_t st);
 
 }  // namespace moe

@@ -14,6 +14,13 @@
 // complemented expert index in the low half, so equal keys go to the lower
 // index).  k rounds pick the experts in slot order; one more round reads the
 // (k+1)-th key for the near-tie count.
+//
+// Group-limited routing (n_group, topk_group of the same Dots1 field table,
+// which maps them to DeepSeek-V3's router): each group's score is the sum of
+// its two largest keys (the table gives no formula; this is DeepSeek-V3's
+// rule).  Lane g computes group g's score from the wave's keys staged in
+// LDS, the same packed-key max picks topk_group groups, and the keys of the
+// experts outside them drop out before the top-k rounds.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -24,10 +31,13 @@ constexpr int kPer = kMaxExperts / 64;
 
 __device__ __forceinline__ float sigmoidf_acc(float l) { return 1.0f / (1.0f + expf(-l)); }
 
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
+constexpr int kWaves = 4;  // waves (tokens) per block
+
+__global__ __launch_bounds__(64 * kWaves) void router_topk_kernel(const float* __restrict__ logits,
                                                           int splits,
                                                           const float* __restrict__ bias, int T,
-                                                          int E, int k, int norm, float rsf,
+                                                          int E, int k, int n_group, int topk_group,
+                                                          int norm, float rsf,
                                                           int32_t* __restrict__ idx_out,
                                                           float* __restrict__ w_out,
                                                           int32_t* __restrict__ ties) {
@@ -39,6 +49,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   const long long split_stride = static_cast<long long>(T) * E;
   float score[kPer];
   uint64_t key[kPer];
+  __shared__ float cbuf[kWaves][kMaxExperts];  // group-limited routing only
+  float* cw = cbuf[threadIdx.x >> 6];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int e = i * 64 + lane;
@@ -49,16 +61,71 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
       score[i] = sigmoidf_acc(l);
       const float c = score[i] + bias[e];
       key[i] = (static_cast<uint64_t>(f32_order_key(c)) << 32) | static_cast<uint32_t>(~e);
+      if (n_group > 1) cw[e] = c;
     } else {
       score[i] = 0.f;
       key[i] = 0;  // below every real key
     }
   }
 
+  // Group limit: group g holds experts [g*G, (g+1)*G); its score is the sum
+  // of its two largest keys.  The topk_group best groups (lower index first
+  // among equal scores) stay; the keys of every other expert drop to 0.
+  int allowed = E;
+  float gap_grp = INFINITY;
+  if (n_group > 1) {
+    // the wave's own LDS row: make the stores visible to the other lanes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int G = E / n_group;
+    uint64_t gkey = 0;
+    if (lane < n_group) {
+      float t1 = -INFINITY, t2 = -INFINITY;
+      for (int j = 0; j < G; ++j) {
+        const float v = cw[lane * G + j];
+        if (v > t1) {
+          t2 = t1;
+          t1 = v;
+        } else if (v > t2) {
+          t2 = v;
+        }
+      }
+      const float gs = (G > 1) ? t1 + t2 : t1;
+      gkey = (static_cast<uint64_t>(f32_order_key(gs)) << 32) | static_cast<uint32_t>(~lane);
+    }
+    uint64_t chosen = 0;
+    float last = 0.f;
+    const int grounds = topk_group < n_group ? topk_group + 1 : topk_group;
+    for (int r = 0; r < grounds; ++r) {
+      uint64_t best = gkey;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const uint64_t o = shfl_xor_u64(best, m);
+        best = o > best ? o : best;
+      }
+      const int g = static_cast<int>(~static_cast<uint32_t>(best));
+      const float sc = f32_from_order_key(static_cast<uint32_t>(best >> 32));
+      if (r < topk_group) {
+        chosen |= 1ull << g;
+        if (lane == g) gkey = 0;
+        last = sc;
+      } else {
+        gap_grp = last - sc;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = i * 64 + lane;
+      if (e < E && !((chosen >> (e / G)) & 1ull)) key[i] = 0;
+    }
+    allowed = topk_group * G;
+  }
+
   int chosen_e[kMaxTopK];
   float chosen_s[kMaxTopK];
   float prev_c = 0.f, min_gap = INFINITY, gap_sel = INFINITY;
-  const int rounds = (k < E) ? k + 1 : k;
+  const int rounds = (k < allowed) ? k + 1 : k;
 #pragma unroll
   for (int j = 0; j <= kMaxTopK; ++j) {
     if (j >= rounds) continue;
@@ -107,7 +174,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     }
   }
   if (ties && lane == 0) {
-    if (gap_sel <= kTieEps) atomicAdd(&ties[0], 1);
+    if (gap_sel <= kTieEps || gap_grp <= kTieEps) atomicAdd(&ties[0], 1);
     if (min_gap <= kTieEps) atomicAdd(&ties[1], 1);
   }
 }
@@ -120,13 +187,13 @@ __global__ void zero_i32_kernel(int32_t* p, int n) {
 }  // namespace
 
 hipError_t launch_router_topk(const float* logits, int splits, const float* bias, int T, int E,
-                              int k, int norm, float rsf, int32_t* idx, float* w, int32_t* ties,
-                              hipStream_t st) {
+                              int k, int n_group, int topk_group, int norm, float rsf, int32_t* idx,
+                              float* w, int32_t* ties, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  const int waves_per_block = 4;
-  const int grid = (T + waves_per_block - 1) / waves_per_block;
-  hipLaunchKernelGGL(router_topk_kernel, dim3(grid), dim3(64 * waves_per_block), 0, st, logits,
-                     splits < 1 ? 1 : splits, bias, T, E, k, norm, rsf, idx, w, ties);
+  const int grid = (T + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(router_topk_kernel, dim3(grid), dim3(64 * kWaves), 0, st, logits,
+                     splits < 1 ? 1 : splits, bias, T, E, k, n_group > 1 ? n_group : 1,
+                     topk_group, norm, rsf, idx, w, ties);
   return hipGetLastError();
 }
 

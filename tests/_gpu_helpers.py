@@ -32,7 +32,10 @@ def out_to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def untied(r) -> np.ndarray:
-    return (r.gap_sel > TIE) & (r.gap_ord > TIE)
+    ok = (r.gap_sel > TIE) & (r.gap_ord > TIE)
+    if r.gap_grp is not None:
+        ok &= r.gap_grp > TIE
+    return ok
 
 
 def check_routing(cfg, r, idx_gpu: np.ndarray, w_gpu: np.ndarray, where: str):
@@ -45,10 +48,12 @@ def check_routing(cfg, r, idx_gpu: np.ndarray, w_gpu: np.ndarray, where: str):
     dw = np.abs(w_gpu[ok] - r.w[ok])
     assert dw.size == 0 or dw.max() <= 1e-6, f"{where}: max |dw| {dw.max():.3e}"
     kth = np.sort(r.keys, axis=1)[:, ::-1][:, cfg.k - 1]
+    grouped = getattr(cfg, "n_group", 1) > 1
     for t in np.nonzero(~ok)[0]:
         row = idx_gpu[t]
         assert len(set(row.tolist())) == cfg.k and row.min() >= 0 and row.max() < cfg.E
-        assert np.all(r.keys[t, row] >= kth[t] - TIE), f"{where}: token {t} invalid top-k"
+        if not grouped:     # with groups, a group near-tie changes the allowed set
+            assert np.all(r.keys[t, row] >= kth[t] - TIE), f"{where}: token {t} invalid top-k"
     return int((~ok).sum())
 
 

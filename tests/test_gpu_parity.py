@@ -46,7 +46,8 @@ def small(**kw):
 def ccfg(cfg):
     return moe.make_config(cfg.T, cfg.H, cfg.E, cfg.S, cfg.k, cfg.I, cfg.Is, act=cfg.act,
                            expert=cfg.expert, norm_topk_prob=cfg.norm_topk_prob,
-                           routed_scaling_factor=cfg.routed_scaling_factor)
+                           routed_scaling_factor=cfg.routed_scaling_factor,
+                           n_group=cfg.n_group, topk_group=cfg.topk_group)
 
 
 def workspace(c):
