@@ -16,6 +16,10 @@ Extra objects in the line:
                summary when its kernel source hash still matches.
   decode_T256  the same layer at T=256 tokens (weight streaming): time,
                algorithmic HBM GB/s and its fraction of 8 TB/s.
+  grouped_routing  the router (logits GEMM + selection) with group-limited
+               routing (8 groups, 4 chosen) next to the plain router.
+  block        the decoder block around the layer (RMSNorm, layer, residual
+               add in the combine) and the RMSNorm kernel alone against HBM.
   cpu_baseline the fp64 CPU oracle on the first tokens of the same workload.
 """
 from __future__ import annotations
@@ -149,6 +153,68 @@ def time_layer(lay, steps, warmup, timed_events=True):
     return wall * 1e3 / steps, step_ev, stage, counts.cpu().numpy()
 
 
+def time_calls(fn, iters, warmup):
+    """Mean ms per call of `fn`, timed with events on torch's current stream
+    (the stream the library launches on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def grouped_routing(lay, cfg, n_group=8, topk_group=4, iters=20):
+    """Router time with and without the group limit on the same inputs."""
+    import torch
+    import sparse_moe_expert_amd as moe
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    cg = moe.make_config(cfg.T, cfg.H, cfg.E, cfg.S, cfg.k, cfg.I, cfg.Is, act=cfg.act,
+                         expert=cfg.expert, n_group=n_group, topk_group=topk_group)
+    ws = torch.empty(moe.moe_workspace_size(cg), dtype=torch.uint8, device="cuda")
+    x = lay.t["x"]
+    plain = time_calls(lambda: moe.moe_route(lay.ccfg, x, lay.weights, idx, tw, None,
+                                             lay.workspace), iters, 3)
+    grouped = time_calls(lambda: moe.moe_route(cg, x, lay.weights, idx, tw, None, ws), iters, 3)
+    torch.cuda.synchronize()
+    groups = (idx.cpu().numpy() // (cfg.E // n_group))
+    return {"n_group": n_group, "topk_group": topk_group, "route_ms": round(grouped, 4),
+            "plain_route_ms": round(plain, 4),
+            "max_groups_per_token": int(max(len(set(r.tolist())) for r in groups))}
+
+
+def block_forward(lay, cfg, steps, layer_ms):
+    """The decoder block (RMSNorm -> layer -> residual) and the RMSNorm kernel
+    alone: its algorithmic bytes (read h and gamma, write the normalised rows)
+    over its time."""
+    import numpy as np
+    import torch
+    import sparse_moe_expert_amd as moe
+    from sparse_moe_expert_amd.device import to_device
+    g = 1.0 + 0.1 * np.random.default_rng(5).standard_normal(cfg.H)
+    gamma = to_device(g.astype(np.float32), "f32").to(lay.act_dtype)
+    out = lay.empty_out()
+    xn = lay.empty_out()
+    h = lay.t["x"]
+    eps = cfg.rms_norm_eps
+    blk = time_calls(lambda: moe.moe_block_forward(lay.ccfg, lay.weights, h, gamma, eps, out,
+                                                   None, None, lay.workspace), steps, 3)
+    norm = time_calls(lambda: moe.moe_rmsnorm(lay.ccfg, h, gamma, eps, xn), 50, 5)
+    asz = h.element_size()
+    nbytes = 2.0 * cfg.T * cfg.H * asz + cfg.H * asz
+    gbs = nbytes / (norm / 1e3) / 1e9
+    return {"ms_per_step": round(blk, 4), "tokens_per_s": round(cfg.T / (blk / 1e3), 1),
+            "overhead_vs_layer_ms": round(blk - layer_ms, 4),
+            "rmsnorm": {"kernel_ms": round(norm, 4), "bytes_per_launch": nbytes,
+                        "achieved_GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def cpu_baseline(cfg, inp, n_tokens):
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -175,7 +241,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-decode", action="store_true", help="skip the T=256 line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=24)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the grouped-routing and block lines")
+    ap.add_argument("--cpu-tokens", type=int, default=512)
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run one plain device-to-device copy of this many GiB "
                          "(calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -252,6 +320,11 @@ def main():
             "stages_ms": {k: round(v, 4) for k, v in stage1.items()},
             "experts_touched": int((counts1 > 0).sum()),
         }
+
+    if not args.no_extras and args.config == 2:
+        log("bench: grouped routing and block forward")
+        res["grouped_routing"] = grouped_routing(lay, cfg)
+        res["block"] = block_forward(lay, cfg, min(args.steps, 10), ms_ev)
 
     if args.calib_copy_gib > 0:
         n = int(args.calib_copy_gib * (1 << 30))
