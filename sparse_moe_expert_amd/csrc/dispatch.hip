@@ -66,15 +66,21 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
                                                              int32_t* __restrict__ chunk_base,
                                                              int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ offsets) {
+  // Thread e walks expert e's column of chunk counts twice (total, then the
+  // running bases).  Loads go out 16 chunks at a time so that their latencies
+  // overlap instead of adding up chunk by chunk.
+  constexpr int B = 16;
   __shared__ int sh[1024];
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      const long long i = static_cast<long long>(c) * E + e;
-      const int v = chunk_counts[i];
-      chunk_base[i] = run;
-      run += v;
+    for (int c0 = 0; c0 < nchunks; c0 += B) {
+      int v[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j)
+        v[j] = (c0 + j < nchunks) ? chunk_counts[static_cast<long long>(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < B; ++j) run += v[j];
     }
   }
   int total = 0;
@@ -82,7 +88,18 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
   if (e < E) {
     counts[e] = run;
     offsets[e] = excl;
-    for (int c = 0; c < nchunks; ++c) chunk_base[static_cast<long long>(c) * E + e] += excl;
+    int acc = excl;
+    for (int c0 = 0; c0 < nchunks; c0 += B) {
+      int v[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j)
+        v[j] = (c0 + j < nchunks) ? chunk_counts[static_cast<long long>(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        if (c0 + j < nchunks) chunk_base[static_cast<long long>(c0 + j) * E + e] = acc;
+        acc += v[j];
+      }
+    }
   }
   if (e == 0) offsets[E] = total;
 }

@@ -444,9 +444,9 @@ hipError_t launch_shape(TileShape ts, const GemmLaunch& g, hipStream_t st) {
 hipError_t launch_gemm(int a_kind, int out_kind, TileShape ts, const GemmLaunch& g,
                        hipStream_t st) {
   const bool dual = g.dual != 0;
-  const bool split = g.k_splits > 1;  // only the generic kernel splits K
+  const bool split = g.k_splits > 1;  // the generic and large-tile kernels split K
   if (split && (out_kind != K_F32 || dual)) return hipErrorInvalidValue;
-  if (!split && gemm_big_supported(a_kind, out_kind, ts, dual))
+  if (gemm_big_supported(a_kind, out_kind, ts, dual))
     return launch_gemm_big(a_kind, out_kind, dual, g, st);
   if (!split && gemm_decode_supported(a_kind, out_kind, ts, dual))
     return launch_gemm_decode(ts, dual, g, st);

@@ -104,7 +104,18 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
   // wave index is uniform across the wave: keep it (and what derives from it) scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = p.K;
-  const int nk = K / KE;
+  int nk = K / KE;
+  // split K (projection with fp32 output): this block's K-slices [kt0, kt0 + nk)
+  // go to C + blockIdx.y * c_split_stride
+  int kt0 = 0;
+  if (p.k_splits > 1) {
+    nk /= p.k_splits;
+    kt0 = blockIdx.y * nk;
+    if constexpr (OK == K_F32) {
+      p.C = static_cast<float*>(p.C) + blockIdx.y * p.c_split_stride;
+      p.C2 = static_cast<float*>(p.C2) + blockIdx.y * p.c_split_stride;
+    }
+  }
   const int N = p.N;
   const long long rowb_a = p.lda * ESZ;
   const long long rowb_b = static_cast<long long>(K) * ESZ;
@@ -189,7 +200,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
   };
   auto issue = [&](int kt) {
     char* base = smem + (kt % NS) * STAGE;
-    const int koff = kt * 128;
+    const int koff = (kt0 + kt) * 128;
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i) dma16(a_src[i] + koff, base + (i * WAVES + wave) * 1024);
 #pragma unroll
@@ -197,8 +208,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
       dma16(job.W + b_off[i] + koff, base + A_BYTES + (i * WAVES + wave) * 1024);
     if constexpr (AK == K_FP8) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) sa_next[tt] = p.a_scale[sa_off[tt] + kt];
-      load_sb(kt);
+      for (int tt = 0; tt < 2; ++tt) sa_next[tt] = p.a_scale[sa_off[tt] + kt0 + kt];
+      load_sb(kt0 + kt);
     }
   };
 
@@ -449,7 +460,8 @@ hipError_t launch_big(const GemmLaunch& g, hipStream_t st) {
   if (total <= 0) return hipSuccess;
   const long long grid = ((total + 7) / 8) * 8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_big_kernel<AK, OK, DUAL>), dim3(static_cast<unsigned>(grid)),
+  const unsigned splits = g.k_splits > 1 ? static_cast<unsigned>(g.k_splits) : 1u;
+  hipLaunchKernelGGL((gemm_big_kernel<AK, OK, DUAL>), dim3(static_cast<unsigned>(grid), splits),
                      dim3(THREADS), 0, st, g);
   return hipGetLastError();
 }

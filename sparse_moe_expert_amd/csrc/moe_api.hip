@@ -318,7 +318,17 @@ Layout make_layout(const moe_config_t& c) {
   L.router = TileShape{T <= 2048 ? 16 : 64, 64};
   L.router_splits = 1;
   if (c.act_dtype == MOE_BF16 && T >= 4096) {
-    L.router = TileShape{128, 512};  // gemm_big.hip
+    L.router = TileShape{128, 512};  // gemm_big.hip: one 512-row weight tile
+    // 128-row tiles leave most CUs idle at this T: split K up to 8 ways, to
+    // about two blocks per CU, keeping >= 8 K-slices per block
+    const size_t tiles = (T + 127) / 128;
+    const int nk = static_cast<int>(H * asz / 128);
+    for (int d = 8; d > 1; --d) {
+      if (nk % d == 0 && nk / d >= 8 && tiles * d <= 512) {
+        L.router_splits = d;
+        break;
+      }
+    }
   } else {
     // Few output tiles (small T): split K so that the launch fills the chip.
     // The partial sums are added in split order by the top-k kernel.

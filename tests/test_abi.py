@@ -89,8 +89,10 @@ def test_workspace_size_covers_buffers():
     c = moe.make_config(T=16384, H=5120, E=256, S=1, k=8, I=1536)
     n = moe.moe_workspace_size(c)
     R = 16384 * 8
-    # h (bf16) + y_sorted and y_shared (fp32) + router logits (fp32)
-    need = (R + 16384) * 1536 * 2 + R * 5120 * 4 + 16384 * 5120 * 4 + 16384 * 256 * 4
+    # h (bf16) + y_sorted and y_shared (fp32) + router logits (fp32, K split
+    # 4 ways at this T) + the normalised block input (bf16)
+    need = ((R + 16384) * 1536 * 2 + R * 5120 * 4 + 16384 * 5120 * 4 + 4 * 16384 * 256 * 4
+            + 16384 * 5120 * 2)
     assert need <= n < need * 1.05
 
 
@@ -138,6 +140,40 @@ def test_validation_rejects_before_launch():
     assert call("moe_dispatch", by(c), FAKE, None, FAKE, FAKE, FAKE, FAKE, n, None) == moe.MOE_ERR_INVALID_ARG
     assert call("moe_quantize_fp8", FAKE, 4, 100, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert call("moe_quantize_fp8", FAKE + 8, 4, 128, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    # decoder block: eps, gamma, aliasing
+    f = ctypes.c_float
+    assert call("moe_rmsnorm", by(c), FAKE, FAKE, f(-1.0), FAKE + 4096, None) == moe.MOE_ERR_INVALID_ARG
+    assert call("moe_rmsnorm", by(c), FAKE, FAKE, f(float("inf")), FAKE + 4096, None) == moe.MOE_ERR_INVALID_ARG
+    assert call("moe_rmsnorm", by(c), FAKE, None, f(1e-6), FAKE + 4096, None) == moe.MOE_ERR_INVALID_ARG
+    assert call("moe_rmsnorm", by(c), FAKE, FAKE, f(1e-6), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert call("moe_rmsnorm", by(c), FAKE + 8, FAKE, f(1e-6), FAKE + 4096, None) == moe.MOE_ERR_INVALID_ARG
+    assert call("moe_block_forward", by(c), by(w), FAKE, FAKE, f(float("nan")), FAKE + 4096, None,
+                None, FAKE, n, None) == moe.MOE_ERR_INVALID_ARG
+    assert call("moe_block_forward", by(c), by(w), FAKE, None, f(1e-6), FAKE + 4096, None, None,
+                FAKE, n, None) == moe.MOE_ERR_INVALID_ARG
+    assert call("moe_block_forward", by(c), by(w), FAKE, FAKE, f(1e-6), FAKE, None, None,
+                FAKE, n, None) == moe.MOE_ERR_INVALID_ARG
+    assert call("moe_block_forward", by(c), by(w), FAKE, FAKE, f(1e-6), FAKE + 4096, None, None,
+                FAKE, n - 1, None) == moe.MOE_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("n_group,topk_group,k,ok", [
+    (0, 0, 4, True), (1, 1, 4, True), (8, 4, 8, True), (32, 32, 4, True), (4, 1, 8, True),
+    (3, 1, 4, False), (8, 0, 4, False), (8, 9, 4, False), (8, 1, 9, False), (-1, 1, 4, False),
+    (64, 4, 4, None),
+])
+def test_group_fields_validate(n_group, topk_group, k, ok):
+    """n_group must divide E with topk_group in 1..n_group and k within the
+    chosen groups; more than 64 groups is unsupported."""
+    c = cfg(E=64 if n_group == 64 else 32, k=k)
+    c.n_group, c.topk_group = n_group, topk_group
+    n = moe.moe_workspace_size(c)
+    if ok is None:
+        assert n > 0
+        c.E, c.n_group = 128, 128
+        assert moe.moe_workspace_size(c) == 0
+        return
+    assert (n > 0) == ok
 
 
 def test_zero_tokens_is_a_noop():
