@@ -15,7 +15,8 @@ Extra objects in the line:
                bf16 MFMA peak; traffic from the committed rocprofv3 counter
                summary when its kernel source hash still matches.
   decode_T256  the same layer at T=256 tokens (weight streaming): time,
-               algorithmic HBM GB/s and its fraction of 8 TB/s.
+               algorithmic HBM GB/s and its fraction of 8 TB/s; also as
+               one cooperative launch (moe_layer_forward_fused).
   grouped_routing  the router (logits GEMM + selection) with group-limited
                routing (8 groups, 4 chosen) next to the plain router.
   block        the decoder block around the layer (RMSNorm, layer, residual
@@ -311,8 +312,17 @@ def main():
         ms1, _, stage1, counts1 = time_layer(lay1, args.decode_steps, 5)
         b1 = layer_bytes(cfg1, counts1)
         gbs = b1 / (ms1 / 1e3) / 1e9
+        # the same layer as one cooperative launch
+        import sparse_moe_expert_amd as moe
+        out1 = lay1.empty_out()
+        msf = time_calls(lambda: moe.moe_layer_forward_fused(
+            lay1.ccfg, lay1.weights, lay1.t["x"], out1, None, None, lay1.workspace),
+            args.decode_steps, 5)
+        gbf = b1 / (msf / 1e3) / 1e9
         res["decode_T256"] = {
             "workload": cfg1.name, "ms_per_step": round(ms1, 4),
+            "fused_single_launch": {"ms_per_step": round(msf, 4), "hbm_GBps": round(gbf, 1),
+                                    "frac_of_hbm_peak": round(gbf / PEAK_HBM_GBS, 4)},
             "tokens_per_s": round(cfg1.T / (ms1 / 1e3), 1),
             "algorithmic_bytes": b1, "hbm_GBps": round(gbs, 1),
             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),

@@ -218,6 +218,22 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
                                void* out, int32_t* opt_counts, int32_t* opt_tie_counts,
                                void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
+/* The whole layer in ONE launch, for the decode regime: the chain route ->
+ * dispatch -> gate/up + SwiGLU -> down -> combine that the Ascend adaptation
+ * figure [DD §8.2, FUSED_MC2] runs as one fused operator.  A cooperative
+ * persistent grid runs the steps as phases separated by grid barriers.
+ * Same arguments, outputs and workspace as moe_layer_forward, and the same
+ * results up to the summation order of the router logits (a near-tie can
+ * pick the other equally valid expert).  Supported where the layer streams
+ * weights: bf16 activations and experts, at most 12 routed rows per expert
+ * on average (T*k/E), E a multiple of 16; otherwise MOE_ERR_UNSUPPORTED and
+ * nothing is enqueued.  The device must hold the whole grid at once
+ * (checked by the cooperative launch; MOE_ERR_HIP if it cannot). */
+moe_status_t moe_layer_forward_fused(const moe_config_t* cfg, const moe_weights_t* w,
+                                     const void* x, void* out, int32_t* opt_counts,
+                                     int32_t* opt_tie_counts, void* workspace,
+                                     size_t workspace_bytes, moe_stream_t stream);
+
 /* RMSNorm of the decoder block [DD §3.3 figure "Residual + RMSNorm"; D1:
  * variance in fp32, rsqrt, times the weight]: for every row t of h [T, H]
  *   out[t, c] = gamma[c] * h[t, c] / sqrt(mean_c' h[t, c']^2 + eps)

@@ -16,7 +16,7 @@ _BINDING = (
     "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_F32", "MOE_FP8_E4M3", "MOE_OK", "MoEError",
     "make_config", "make_weights", "moe_combine", "moe_config_t", "moe_dispatch",
     "moe_expert_down", "moe_expert_gate_up", "moe_grouped_ffn", "moe_layer_forward",
-    "moe_layer_forward_timed", "moe_rmsnorm", "moe_block_forward",
+    "moe_layer_forward_timed", "moe_rmsnorm", "moe_block_forward", "moe_layer_forward_fused",
     "moe_quantize_fp8", "moe_route", "moe_weights_t", "moe_workspace_size", "status_string",
     "version", "last_error_detail",
 )

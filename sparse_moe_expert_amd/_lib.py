@@ -21,7 +21,7 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_version", "moe_workspace_size", "moe_route",
            "moe_dispatch", "moe_grouped_ffn", "moe_expert_gate_up", "moe_expert_down",
            "moe_combine", "moe_quantize_fp8", "moe_layer_forward", "moe_layer_forward_timed",
-           "moe_rmsnorm", "moe_block_forward")
+           "moe_rmsnorm", "moe_block_forward", "moe_layer_forward_fused")
 
 
 class MoEError(RuntimeError):
@@ -75,6 +75,7 @@ def _load():
         "moe_layer_forward": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P, SZ, P]),
         "moe_layer_forward_timed": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P, SZ, P,
                                                    ctypes.POINTER(ctypes.c_void_p)]),
+        "moe_layer_forward_fused": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P, SZ, P]),
         "moe_rmsnorm": (ctypes.c_int, [CP, P, P, ctypes.c_float, P, P]),
         "moe_block_forward": (ctypes.c_int, [CP, WP, P, P, ctypes.c_float, P, I32P, I32P, P, SZ,
                                              P]),
@@ -209,6 +210,14 @@ def moe_layer_forward_timed(cfg, weights, x, out, events, opt_counts=None, opt_t
     _check(LIB.moe_layer_forward_timed(ctypes.byref(cfg), ctypes.byref(weights), _ptr(x),
                                        _ptr(out), _ptr(opt_counts), _ptr(opt_tie_counts), wp, wb,
                                        _stream(stream), arr), "moe_layer_forward_timed")
+
+
+def moe_layer_forward_fused(cfg, weights, x, out, opt_counts=None, opt_tie_counts=None,
+                            workspace=None, stream=None):
+    wp, wb = _ws(workspace)
+    _check(LIB.moe_layer_forward_fused(ctypes.byref(cfg), ctypes.byref(weights), _ptr(x),
+                                       _ptr(out), _ptr(opt_counts), _ptr(opt_tie_counts), wp, wb,
+                                       _stream(stream)), "moe_layer_forward_fused")
 
 
 def moe_rmsnorm(cfg, h, gamma, eps, out, stream=None):

@@ -12,8 +12,7 @@
 // all-zero block) and code = e4m3(v / scale), round to nearest even -- the
 // FP8 format of "dots3-note 架构深度解析" (mlqm.cn, «核心架构参数一览»:
 // BF16、FP8) at per-token-per-128-channel granularity.
-#include "moe_device.h"
-#include "moe_internal.h"
+#include "combine_device.h"
 
 namespace moe {
 namespace {
@@ -28,52 +27,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       int S) {
   __shared__ float ws[kMaxTopK];
   __shared__ long long rs[kMaxTopK];
-  const int t = blockIdx.x;
-  if (threadIdx.x < k) {
-    ws[threadIdx.x] = w[static_cast<long long>(t) * k + threadIdx.x];
-    rs[threadIdx.x] = inv[static_cast<long long>(t) * k + threadIdx.x];
-  }
-  __syncthreads();
-  for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
-    float4 acc = float4{0.f, 0.f, 0.f, 0.f};
-    if (residual) {
-      // decoder block: the residual stream comes first
-      if constexpr (OK == K_BF16) {
-        const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(residual) +
-                                                        static_cast<long long>(t) * H + c);
-        acc = float4{bf16_to_f32(static_cast<uint16_t>(r.x & 0xFFFF)),
-                     bf16_to_f32(static_cast<uint16_t>(r.x >> 16)),
-                     bf16_to_f32(static_cast<uint16_t>(r.y & 0xFFFF)),
-                     bf16_to_f32(static_cast<uint16_t>(r.y >> 16))};
-      } else {
-        acc = *reinterpret_cast<const float4*>(static_cast<const float*>(residual) +
-                                               static_cast<long long>(t) * H + c);
-      }
-    }
-    for (int s = 0; s < S; ++s) {
-      const float4 v = *reinterpret_cast<const float4*>(ysh + (static_cast<long long>(s) * T + t) * H + c);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
-    }
-    for (int j = 0; j < k; ++j) {
-      const float wj = ws[j];
-      const float4 v = *reinterpret_cast<const float4*>(y + rs[j] * H + c);
-      acc.x = fmaf(wj, v.x, acc.x);
-      acc.y = fmaf(wj, v.y, acc.y);
-      acc.z = fmaf(wj, v.z, acc.z);
-      acc.w = fmaf(wj, v.w, acc.w);
-    }
-    if constexpr (OK == K_BF16) {
-      uint2 o;
-      o.x = f32_to_bf16(acc.x) | (static_cast<uint32_t>(f32_to_bf16(acc.y)) << 16);
-      o.y = f32_to_bf16(acc.z) | (static_cast<uint32_t>(f32_to_bf16(acc.w)) << 16);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + static_cast<long long>(t) * H + c) = o;
-    } else {
-      *reinterpret_cast<float4*>(static_cast<float*>(out) + static_cast<long long>(t) * H + c) = acc;
-    }
-  }
+  combine_token<OK>(y, ysh, w, inv, residual, out, T, H, k, S, blockIdx.x, ws, rs);
 }
 
 // 16 lanes per 128-channel block, 8 channels per lane.

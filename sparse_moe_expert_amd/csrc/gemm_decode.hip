@@ -21,132 +21,14 @@
 //  * The expert's token rows (A) come from L2: all waves of the expert read
 //    the same few rows.
 //  * v_mfma_f32_16x16x32_bf16: rows = tokens (lane%16), columns = weight rows.
-#include "gemm_sched.h"
+#include "gemm_decode_device.h"
 
 namespace moe {
 namespace {
 
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-template <int MT, int NT>
-struct Regs {
-  uint4 a[MT][4];
-  uint4 b[NT][4];
-};
-
 template <int MT, bool DUAL, int NT>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmLaunch p) {
-  // NT 16-row weight tiles per wave: gate/up holds NT/2 gate tiles and the
-  // NT/2 matching up tiles
-  constexpr int BM = 16 * MT;
-  constexpr int WC = DUAL ? 8 * NT : 16 * NT;  // output columns per wave
-  constexpr int BN = 4 * WC;                   // per block (4 waves)
-  TileJob job;
-  if (!find_tile<BM, BN, DUAL>(p, job)) return;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int lrow = lane & 15;
-  const int lgrp = lane >> 4;
-  const int K = p.K;
-  const int N = p.N;
-  const int nkb = K / 128;
-  const long long rowb_a = p.lda * 2;
-  const long long rowb_b = static_cast<long long>(K) * 2;
-
-  // this wave's weight rows
-  const int wn0 = job.n0 + wave * WC;
-  const char* bptr[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    int wr;
-    if constexpr (DUAL) {
-      // tiles [0, NT/2) gate rows, [NT/2, NT) the matching up rows
-      const int n = min(wn0 + (t % (NT / 2)) * 16 + lrow, N - 1);
-      wr = (t < NT / 2) ? n : N + n;
-    } else {
-      wr = min(wn0 + t * 16 + lrow, N - 1);
-    }
-    bptr[t] = job.W + wr * rowb_b + lgrp * 16;
-  }
-  const char* aptr[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const int r = min(m * 16 + lrow, job.rows_here - 1);
-    const int src = gemm_a_source_row(p, job.row_begin + job.m0 + r);
-    aptr[m] = static_cast<const char*>(p.A) + src * rowb_a + lgrp * 16;
-  }
-
-  auto load = [&](Regs<MT, NT>& R, int kb) {
-    const int off = kb * 256;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) R.b[t][s] = *reinterpret_cast<const uint4*>(bptr[t] + off + s * 64);
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) R.a[m][s] = *reinterpret_cast<const uint4*>(aptr[m] + off + s * 64);
-  };
-
-  f32x4_t acc[MT][NT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[m][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](const Regs<MT, NT>& R) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, R.a[m][s]), __builtin_bit_cast(bf16x8, R.b[t][s]),
-              acc[m][t], 0, 0, 0);
-  };
-
-  Regs<MT, NT> r0, r1;
-  load(r0, 0);
-  int kb = 0;
-  for (; kb + 2 <= nkb; kb += 2) {
-    load(r1, kb + 1);
-    compute(r0);
-    if (kb + 2 < nkb) load(r0, kb + 2);
-    compute(r1);
-  }
-  if (kb < nkb) compute(r0);
-
-  // 16x16 accumulator layout: lane l, element i -> token row 4*(l/16) + i,
-  // weight row l%16 of the tile.
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = m * 16 + lgrp * 4 + i;
-      if (r >= job.rows_here) continue;
-      const long long row = job.row_begin + job.m0 + r;
-      if constexpr (DUAL) {
-#pragma unroll
-        for (int j = 0; j < NT / 2; ++j) {
-          const int n = wn0 + j * 16 + lrow;
-          if (n < N) {
-            const float g = acc[m][j][i];
-            const float u = acc[m][j + NT / 2][i];
-            reinterpret_cast<uint16_t*>(gemm_out_row<2>(p, row))[n] =
-                f32_to_bf16(g / (1.0f + expf(-g)) * u);
-          }
-        }
-      } else {
-        float* dst = reinterpret_cast<float*>(gemm_out_row<4>(p, row));
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const int n = wn0 + t * 16 + lrow;
-          if (n < N) dst[n] = acc[m][t][i];
-        }
-      }
-    }
+  decode_tile<MT, DUAL, NT>(p, blockIdx.x);
 }
 
 template <int MT, bool DUAL, int NT>

@@ -22,16 +22,18 @@ struct TileJob {
 // the tile list: consecutive tiles then share that XCD's L2.  Returns false
 // if the block has no tile.  Tiles run group by group; inside a group n-tile
 // major, m-tile minor.
+// `b` is the block index (blockIdx.x, or a virtual block of a persistent
+// grid whose size is a multiple of 8, which keeps b % 8 the XCD).
 template <int BM, int BN, bool DUAL>
-__device__ __forceinline__ bool find_tile(const GemmLaunch& p, TileJob& job) {
+__device__ __forceinline__ bool find_tile_at(const GemmLaunch& p, TileJob& job, int b) {
   const int ntn = (p.N + BN - 1) / BN;
   const int total_m =
       p.single_group_rows > 0 ? (p.single_group_rows + BM - 1) / BM : *p.total_mtiles;
   const int total = total_m * ntn;
   const int per_xcd = (total + 7) >> 3;
-  const int slot = blockIdx.x >> 3;
+  const int slot = b >> 3;
   if (slot >= per_xcd) return false;
-  const int w_id = (blockIdx.x & 7) * per_xcd + slot;
+  const int w_id = (b & 7) * per_xcd + slot;
   if (w_id >= total) return false;
   int mt = w_id / ntn;
   int nt = w_id - mt * ntn;
@@ -67,6 +69,11 @@ __device__ __forceinline__ bool find_tile(const GemmLaunch& p, TileJob& job) {
   job.rows_here = min(BM, job.rows_here - job.m0);
   job.n0 = nt * BN;
   return true;
+}
+
+template <int BM, int BN, bool DUAL>
+__device__ __forceinline__ bool find_tile(const GemmLaunch& p, TileJob& job) {
+  return find_tile_at<BM, BN, DUAL>(p, job, blockIdx.x);
 }
 
 __device__ __forceinline__ int gemm_a_source_row(const GemmLaunch& p, int row) {

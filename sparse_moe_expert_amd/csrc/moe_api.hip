@@ -153,8 +153,8 @@ hipError_t run_quant_x(const moe_config_t& c, const Layout& L, const void* x, vo
                                at<float>(ws, L.xs), st);
 }
 
-hipError_t run_gate_up_gemm(const moe_config_t& c, const Layout& L, const void* x,
-                            const int32_t* perm, void* ws, hipStream_t st) {
+GemmLaunch gate_up_launch(const moe_config_t& c, const Layout& L, const void* x,
+                          const int32_t* perm, void* ws) {
   const bool fp8 = is_fp8(c);
   GemmLaunch g{};
   g.groups = at<GroupDesc>(ws, L.groups);
@@ -176,7 +176,13 @@ hipError_t run_gate_up_gemm(const moe_config_t& c, const Layout& L, const void* 
   g.c_split = LLONG_MAX;
   g.ldc = c.I;
   g.c_scale = fp8 ? at<float>(ws, L.hs) : nullptr;
-  return launch_gemm(expert_kind(c), fp8 ? K_FP8 : act_kind(c), L.gu, g, st);
+  return g;
+}
+
+hipError_t run_gate_up_gemm(const moe_config_t& c, const Layout& L, const void* x,
+                            const int32_t* perm, void* ws, hipStream_t st) {
+  return launch_gemm(expert_kind(c), is_fp8(c) ? K_FP8 : act_kind(c), L.gu,
+                     gate_up_launch(c, L, x, perm, ws), st);
 }
 
 hipError_t run_gate_up(const moe_config_t& c, const Layout& L, const void* x, const int32_t* perm,
@@ -259,8 +265,8 @@ moe_status_t layer_impl(const moe_config_t* cfg, const moe_weights_t* w, const v
                               static_cast<hipStream_t>(stream), events));
 }
 
-hipError_t run_down(const moe_config_t& c, const Layout& L, void* y_sorted, void* y_shared,
-                    void* ws, hipStream_t st) {
+GemmLaunch down_launch(const moe_config_t& c, const Layout& L, void* y_sorted, void* y_shared,
+                       void* ws) {
   const bool fp8 = is_fp8(c);
   GemmLaunch g{};
   g.groups = at<GroupDesc>(ws, L.groups);
@@ -281,7 +287,12 @@ hipError_t run_down(const moe_config_t& c, const Layout& L, void* y_sorted, void
   g.C2 = y_shared;
   g.c_split = static_cast<long long>(c.T) * c.k;
   g.ldc = c.H;
-  return launch_gemm(expert_kind(c), K_F32, L.dn, g, st);
+  return g;
+}
+
+hipError_t run_down(const moe_config_t& c, const Layout& L, void* y_sorted, void* y_shared,
+                    void* ws, hipStream_t st) {
+  return launch_gemm(expert_kind(c), K_F32, L.dn, down_launch(c, L, y_sorted, y_shared, ws), st);
 }
 
 }  // namespace
@@ -523,6 +534,61 @@ moe_status_t moe_layer_forward_timed(const moe_config_t* cfg, const moe_weights_
   if (!events) return MOE_ERR_INVALID_ARG;
   return layer_impl(cfg, w, x, out, opt_counts, opt_tie_counts, workspace, workspace_bytes, stream,
                     events);
+}
+
+moe_status_t moe_layer_forward_fused(const moe_config_t* cfg, const moe_weights_t* w,
+                                     const void* x, void* out, int32_t* opt_counts,
+                                     int32_t* opt_tie_counts, void* workspace,
+                                     size_t workspace_bytes, moe_stream_t stream) {
+  moe_status_t s = check_layer_args(cfg, w, x, out, workspace, workspace_bytes, nullptr);
+  if (s != MOE_OK || cfg->T == 0) return s;
+  const moe_config_t& c = *cfg;
+  const Layout L = make_layout(c);
+  if (c.act_dtype != MOE_BF16 || c.expert_dtype != MOE_BF16 || !fused_decode_supported(L.gu, L.dn))
+    return MOE_ERR_UNSUPPORTED;
+  if (c.E % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  int splits = L.router_splits;
+  if ((c.H / splits) % 32 != 0) splits = 1;
+  void* ws = workspace;
+  FusedArgs a{};
+  a.T = c.T;
+  a.H = c.H;
+  a.E = c.E;
+  a.S = c.S;
+  a.k = c.k;
+  a.I = c.I;
+  a.n_group = c.n_group > 1 ? c.n_group : 1;
+  a.topk_group = c.topk_group;
+  a.norm = c.norm_topk_prob;
+  a.rsf = c.routed_scaling_factor;
+  a.x = static_cast<const uint16_t*>(x);
+  a.w_router = static_cast<const uint16_t*>(w->w_router);
+  a.bias = w->router_bias;
+  a.logits = at<float>(ws, L.logits);
+  a.splits = splits;
+  a.idx = at<int32_t>(ws, L.topk_idx);
+  a.tw = at<float>(ws, L.topk_w);
+  a.ties = opt_tie_counts;
+  a.counts = opt_counts ? opt_counts : at<int32_t>(ws, L.counts);
+  a.offsets = at<int32_t>(ws, L.offsets);
+  a.perm = at<int32_t>(ws, L.perm);
+  a.inv = at<int32_t>(ws, L.inv);
+  a.groups = at<GroupDesc>(ws, L.groups);
+  a.totals = at<int32_t>(ws, L.totals);
+  a.w_gu = static_cast<const char*>(w->w_gate_up);
+  a.w_dn = static_cast<const char*>(w->w_down);
+  a.w_sh_gu = static_cast<const char*>(w->w_sh_gate_up);
+  a.w_sh_dn = static_cast<const char*>(w->w_sh_down);
+  a.tgu = L.gu;
+  a.tdn = L.dn;
+  a.gu = gate_up_launch(c, L, x, a.perm, ws);
+  a.dn = down_launch(c, L, at<char>(ws, L.y), at<char>(ws, L.ysh), ws);
+  a.y = at<float>(ws, L.y);
+  a.ysh = at<float>(ws, L.ysh);
+  a.residual = nullptr;
+  a.out = out;
+  clear_stale_error();
+  return hip_status(launch_fused_decode(a, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_rmsnorm(const moe_config_t* cfg, const void* h, const void* gamma, float eps,

@@ -122,6 +122,40 @@ hipError_t launch_gemm_decode(TileShape ts, bool dual, const GemmLaunch& g, hipS
 hipError_t launch_router_topk(const float* logits, int splits, const float* bias, int T, int E,
                               int k, int n_group, int topk_group, int norm, float rsf, int32_t* idx,
                               float* w, int32_t* ties, hipStream_t st);
+// Single-launch layer for the decode regime (fused.hip): one cooperative
+// persistent grid runs router logits, top-k, dispatch and the tile table,
+// both weight-streaming GEMMs and the combine, with grid barriers between.
+struct FusedArgs {
+  int T, H, E, S, k, I, n_group, topk_group, norm;
+  float rsf;
+  const uint16_t* x;         // [T, H] bf16
+  const uint16_t* w_router;  // [E, H] bf16
+  const float* bias;         // [E]
+  float* logits;             // [splits, T, E]
+  int splits;                // K split of the router logits (H / splits % 32 == 0)
+  int32_t* idx;              // [T, k]
+  float* tw;                 // [T, k]
+  int32_t* ties;             // [2] or null
+  int32_t* counts;           // [E]
+  int32_t* offsets;          // [E + 1]
+  int32_t* perm;             // [T*k]
+  int32_t* inv;              // [T*k]
+  GroupDesc* groups;         // [E + S]
+  int32_t* totals;           // [2]: m-tiles of gate/up and down
+  const char* w_gu;
+  const char* w_dn;
+  const char* w_sh_gu;
+  const char* w_sh_dn;
+  TileShape tgu, tdn;        // decode tile shapes (bm 16, NT 4)
+  GemmLaunch gu, dn;         // the two grouped GEMMs (tables above)
+  const float* y;            // [T*k, H] fp32 (= dn.C)
+  const float* ysh;          // [S, T, H] fp32 (= dn.C2)
+  const void* residual;      // null or [T, H] bf16
+  void* out;                 // [T, H] bf16
+};
+bool fused_decode_supported(TileShape gu, TileShape dn);
+hipError_t launch_fused_decode(const FusedArgs& a, hipStream_t st);
+
 // RMSNorm rows of [T, H] (act kind F32 or BF16), fp32 math, one rounding.
 hipError_t launch_rmsnorm(int act_kind, const void* h, const void* gamma, float eps, void* out,
                           int T, int H, hipStream_t st);
