@@ -142,7 +142,8 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __
 
 __global__ __launch_bounds__(1024) void build_groups_kernel(
     const int32_t* __restrict__ offsets, int T, int k, int E, int S, GroupDesc* __restrict__ groups,
-    int32_t* __restrict__ totals, int bm_gu, int bm_dn, const char* w_gu, const float* s_gu,
+    int32_t* __restrict__ totals, int32_t* __restrict__ mtg_gu, int32_t* __restrict__ mtg_dn,
+    int bm_gu, int bm_dn, const char* w_gu, const float* s_gu,
     const char* w_dn, const float* s_dn, const char* w_sh_gu, const float* s_sh_gu,
     const char* w_sh_dn, const float* s_sh_dn, int H, int I, int esz, int fp8) {
   __shared__ int sh[1024];
@@ -178,6 +179,9 @@ __global__ __launch_bounds__(1024) void build_groups_kernel(
     d.s_gu = fp8 ? (shared ? s_sh_gu : s_gu) + e * gu_sc : nullptr;
     d.s_dn = fp8 ? (shared ? s_sh_dn : s_dn) + e * dn_sc : nullptr;
     groups[g] = d;
+    // m-tile -> group tables (the GEMMs look their tile's group up directly)
+    for (int i = 0; i < tg; ++i) mtg_gu[ex_g + i] = g;
+    for (int i = 0; i < td; ++i) mtg_dn[ex_d + i] = g;
   }
   if (g == 0) {
     totals[0] = tot_g;
@@ -188,13 +192,14 @@ __global__ __launch_bounds__(1024) void build_groups_kernel(
 }  // namespace
 
 hipError_t launch_groups_only(const int32_t* offsets, int T, int k, int E, int S,
-                              GroupDesc* groups, int32_t* totals, TileShape gu, TileShape dn,
+                              GroupDesc* groups, int32_t* totals, int32_t* mtg_gu,
+                              int32_t* mtg_dn, TileShape gu, TileShape dn,
                               const void* w_gu, const float* s_gu, const void* w_dn,
                               const float* s_dn, const void* w_sh_gu, const float* s_sh_gu,
                               const void* w_sh_dn, const float* s_sh_dn, int H, int I,
                               int expert_kind, hipStream_t st) {
   hipLaunchKernelGGL(build_groups_kernel, dim3(1), dim3(1024), 0, st, offsets, T, k, E, S, groups,
-                     totals, gu.bm, dn.bm, static_cast<const char*>(w_gu), s_gu,
+                     totals, mtg_gu, mtg_dn, gu.bm, dn.bm, static_cast<const char*>(w_gu), s_gu,
                      static_cast<const char*>(w_dn), s_dn, static_cast<const char*>(w_sh_gu),
                      s_sh_gu, static_cast<const char*>(w_sh_dn), s_sh_dn, H, I,
                      static_cast<int>(kind_size(expert_kind)), expert_kind == K_FP8 ? 1 : 0);
@@ -204,7 +209,8 @@ hipError_t launch_groups_only(const int32_t* offsets, int T, int k, int E, int S
 hipError_t launch_dispatch(const int32_t* topk_idx, int T, int k, int E, int S,
                            int32_t* chunk_counts, int32_t* chunk_base, int nchunks,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                           GroupDesc* groups, int32_t* totals, TileShape gu, TileShape dn,
+                           GroupDesc* groups, int32_t* totals, int32_t* mtg_gu,
+                           int32_t* mtg_dn, TileShape gu, TileShape dn,
                            const void* w_gu, const float* s_gu, const void* w_dn,
                            const float* s_dn, const void* w_sh_gu, const float* s_sh_gu,
                            const void* w_sh_dn, const float* s_sh_dn, int H, int I,
@@ -223,7 +229,8 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int T, int k, int E, int S,
                      nchunks, chunk_base, perm, inv);
   err = hipGetLastError();
   if (err != hipSuccess || groups == nullptr) return err;
-  return launch_groups_only(offsets, T, k, E, S, groups, totals, gu, dn, w_gu, s_gu, w_dn, s_dn,
+  return launch_groups_only(offsets, T, k, E, S, groups, totals, mtg_gu, mtg_dn, gu, dn, w_gu,
+                            s_gu, w_dn, s_dn,
                             w_sh_gu, s_sh_gu, w_sh_dn, s_sh_dn, H, I, expert_kind, st);
 }
 

@@ -192,6 +192,8 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
       d.s_gu = nullptr;
       d.s_dn = nullptr;
       a.groups[gi] = d;
+      for (int i = 0; i < (d.rows + a.tgu.bm - 1) / a.tgu.bm; ++i) a.mtg_gu[d.tile_begin_gu + i] = gi;
+      for (int i = 0; i < (d.rows + a.tdn.bm - 1) / a.tdn.bm; ++i) a.mtg_dn[d.tile_begin_dn + i] = gi;
     }
   }
   grid.sync();

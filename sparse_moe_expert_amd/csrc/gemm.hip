@@ -148,11 +148,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
     W = static_cast<const char*>(p.b_single);
     WS = nullptr;
   } else {
-    int lo = 0, hi = p.num_groups - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      const int tb = DUAL ? p.groups[mid].tile_begin_gu : p.groups[mid].tile_begin_dn;
-      if (tb <= mt) lo = mid; else hi = mid - 1;
+    int lo = 0;
+    if (p.mtile_group) {
+      lo = p.mtile_group[mt];
+    } else {
+      int hi = p.num_groups - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        const int tb = DUAL ? p.groups[mid].tile_begin_gu : p.groups[mid].tile_begin_dn;
+        if (tb <= mt) lo = mid; else hi = mid - 1;
+      }
     }
     const GroupDesc gd = p.groups[lo];
     row_begin = gd.row_begin;

@@ -45,11 +45,16 @@ __device__ __forceinline__ bool find_tile_at(const GemmLaunch& p, TileJob& job, 
     job.W = static_cast<const char*>(p.b_single);
     job.WS = nullptr;
   } else {
-    int lo = 0, hi = p.num_groups - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      const int tb = DUAL ? p.groups[mid].tile_begin_gu : p.groups[mid].tile_begin_dn;
-      if (tb <= mt) lo = mid; else hi = mid - 1;
+    int lo = 0;
+    if (p.mtile_group) {
+      lo = p.mtile_group[mt];
+    } else {
+      int hi = p.num_groups - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        const int tb = DUAL ? p.groups[mid].tile_begin_gu : p.groups[mid].tile_begin_dn;
+        if (tb <= mt) lo = mid; else hi = mid - 1;
+      }
     }
     const GroupDesc gd = p.groups[lo];
     job.row_begin = gd.row_begin;

@@ -141,7 +141,8 @@ hipError_t run_route(const moe_config_t& c, const Layout& L, const void* x, cons
 hipError_t run_groups(const moe_config_t& c, const Layout& L, const int32_t* offsets,
                       const moe_weights_t& w, void* ws, hipStream_t st) {
   return launch_groups_only(offsets, c.T, c.k, c.E, c.S, at<GroupDesc>(ws, L.groups),
-                            at<int32_t>(ws, L.totals), L.gu, L.dn, w.w_gate_up, w.s_gate_up,
+                            at<int32_t>(ws, L.totals), at<int32_t>(ws, L.mtg_gu),
+                            at<int32_t>(ws, L.mtg_dn), L.gu, L.dn, w.w_gate_up, w.s_gate_up,
                             w.w_down, w.s_down, w.w_sh_gate_up, w.s_sh_gate_up, w.w_sh_down,
                             w.s_sh_down, c.H, c.I, expert_kind(c), st);
 }
@@ -162,6 +163,7 @@ GemmLaunch gate_up_launch(const moe_config_t& c, const Layout& L, const void* x,
   g.total_mtiles = at<int32_t>(ws, L.totals);
   g.dual = 1;
   g.grid_mtiles_upper = static_cast<int>(mtiles_upper(c, L.gu.bm));
+  g.mtile_group = at<int32_t>(ws, L.mtg_gu);
   g.N = c.I;
   g.K = c.H;
   g.A = fp8 ? static_cast<const void*>(at<uint8_t>(ws, L.xq)) : x;
@@ -239,7 +241,8 @@ hipError_t layer_run(const moe_config_t& c, const moe_weights_t* w, const void* 
   if (e == hipSuccess)
     e = launch_dispatch(idx, c.T, c.k, c.E, c.S, at<int32_t>(ws, L.chunk_counts),
                         at<int32_t>(ws, L.chunk_base), L.nchunks, counts, offsets, perm, inv,
-                        at<GroupDesc>(ws, L.groups), at<int32_t>(ws, L.totals), L.gu, L.dn,
+                        at<GroupDesc>(ws, L.groups), at<int32_t>(ws, L.totals),
+                        at<int32_t>(ws, L.mtg_gu), at<int32_t>(ws, L.mtg_dn), L.gu, L.dn,
                         w->w_gate_up, w->s_gate_up, w->w_down, w->s_down, w->w_sh_gate_up,
                         w->s_sh_gate_up, w->w_sh_down, w->s_sh_down, c.H, c.I, expert_kind(c), st);
   if (e == hipSuccess) e = record(events, 2, st);
@@ -274,6 +277,7 @@ GemmLaunch down_launch(const moe_config_t& c, const Layout& L, void* y_sorted, v
   g.total_mtiles = at<int32_t>(ws, L.totals) + 1;
   g.dual = 0;
   g.grid_mtiles_upper = static_cast<int>(mtiles_upper(c, L.dn.bm));
+  g.mtile_group = at<int32_t>(ws, L.mtg_dn);
   g.N = c.H;
   g.K = c.I;
   g.A = at<char>(ws, L.h);
@@ -370,6 +374,8 @@ Layout make_layout(const moe_config_t& c) {
   L.chunk_base = take(static_cast<size_t>(L.nchunks) * E * 4);
   L.groups = take((E + S) * sizeof(GroupDesc));
   L.totals = take(16);
+  L.mtg_gu = take(static_cast<size_t>(mtiles_upper(c, L.gu.bm)) * 4);
+  L.mtg_dn = take(static_cast<size_t>(mtiles_upper(c, L.dn.bm)) * 4);
   L.xq = take(fp8 ? T * H : 0);
   L.xs = take(fp8 ? T * (H / kQBlock) * 4 : 0);
   L.h = take(rows_all * I * (fp8 ? 1 : asz));
@@ -436,9 +442,10 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx, int3
   return hip_status(launch_dispatch(topk_idx, c.T, c.k, c.E, c.S,
                                     at<int32_t>(workspace, L.chunk_counts),
                                     at<int32_t>(workspace, L.chunk_base), L.nchunks, counts,
-                                    offsets, perm, inv, nullptr, nullptr, L.gu, L.dn, nullptr,
-                                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                    c.H, c.I, expert_kind(c), static_cast<hipStream_t>(stream)));
+                                    offsets, perm, inv, nullptr, nullptr, nullptr, nullptr, L.gu,
+                                    L.dn, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                    nullptr, nullptr, c.H, c.I, expert_kind(c),
+                                    static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_expert_gate_up(const moe_config_t* cfg, const void* x, const moe_weights_t* w,
@@ -575,6 +582,8 @@ moe_status_t moe_layer_forward_fused(const moe_config_t* cfg, const moe_weights_
   a.inv = at<int32_t>(ws, L.inv);
   a.groups = at<GroupDesc>(ws, L.groups);
   a.totals = at<int32_t>(ws, L.totals);
+  a.mtg_gu = at<int32_t>(ws, L.mtg_gu);
+  a.mtg_dn = at<int32_t>(ws, L.mtg_dn);
   a.w_gu = static_cast<const char*>(w->w_gate_up);
   a.w_dn = static_cast<const char*>(w->w_down);
   a.w_sh_gu = static_cast<const char*>(w->w_sh_gate_up);

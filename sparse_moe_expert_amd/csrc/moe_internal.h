@@ -55,6 +55,8 @@ struct Layout {
   size_t chunk_base;    // [nchunks, E] int32
   size_t groups;        // [E + S] GroupDesc
   size_t totals;        // [4] int32: m-tiles of gate/up, m-tiles of down
+  size_t mtg_gu;        // [m-tile upper bound] int32: group of each gate/up m-tile
+  size_t mtg_dn;        // [m-tile upper bound] int32: group of each down m-tile
   size_t xq;            // FP8: [T, H] e4m3 codes
   size_t xs;            // FP8: [T, H/128] fp32 scales
   size_t h;             // [R + S*T, I] act type, or e4m3 codes (FP8)
@@ -85,6 +87,8 @@ struct GemmLaunch {
                                 // (router), weights in b_single
   const void* b_single;
   int grid_mtiles_upper;        // host upper bound of m-tiles
+  const int32_t* mtile_group;   // group of each m-tile (device), or null:
+                                // then a binary search over the groups
   // shapes
   int N;  // output columns (h columns for the gate/up GEMM)
   int K;  // reduction length
@@ -142,6 +146,8 @@ struct FusedArgs {
   int32_t* inv;              // [T*k]
   GroupDesc* groups;         // [E + S]
   int32_t* totals;           // [2]: m-tiles of gate/up and down
+  int32_t* mtg_gu;           // m-tile -> group tables of the two GEMMs
+  int32_t* mtg_dn;
   const char* w_gu;
   const char* w_dn;
   const char* w_sh_gu;
@@ -164,14 +170,16 @@ hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t st);
 hipError_t launch_dispatch(const int32_t* topk_idx, int T, int k, int E, int S,
                            int32_t* chunk_counts, int32_t* chunk_base, int nchunks,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                           GroupDesc* groups, int32_t* totals, TileShape gu, TileShape dn,
+                           GroupDesc* groups, int32_t* totals, int32_t* mtg_gu, int32_t* mtg_dn,
+                           TileShape gu, TileShape dn,
                            const void* w_gu, const float* s_gu, const void* w_dn,
                            const float* s_dn, const void* w_sh_gu, const float* s_sh_gu,
                            const void* w_sh_dn, const float* s_sh_dn, int H, int I,
                            int expert_kind, hipStream_t st);
 
 hipError_t launch_groups_only(const int32_t* offsets, int T, int k, int E, int S,
-                              GroupDesc* groups, int32_t* totals, TileShape gu, TileShape dn,
+                              GroupDesc* groups, int32_t* totals, int32_t* mtg_gu, int32_t* mtg_dn,
+                           TileShape gu, TileShape dn,
                               const void* w_gu, const float* s_gu, const void* w_dn,
                               const float* s_dn, const void* w_sh_gu, const float* s_sh_gu,
                               const void* w_sh_dn, const float* s_sh_dn, int H, int I,
