@@ -348,7 +348,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
         if constexpr (DUAL) {
           const float g = v;
           const float u = acc[C::NB - 1][tm][tn][i];
-          v = g / (1.0f + __expf(-g)) * u;
+          v = silu_mul(g, u);
         }
         Cs[r * C::LDC + c] = v;
       }

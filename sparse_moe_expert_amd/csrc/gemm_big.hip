@@ -333,7 +333,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
             const int c = (2 * wn8 + (tw >> 2)) * 32 + (tw & 1) * 16 + 4 * (lane >> 4) + i;
             const float g = acc8[tw][tt][i];
             const float u = acc8[tw + 2][tt][i];
-            Cs[tok * LDC + c] = g / (1.0f + expf(-g)) * u;
+            Cs[tok * LDC + c] = silu_mul(g, u);
           }
       }
       __syncthreads();
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
         const int c = wn * 32 + lrow;
         const float g = acc[tm][0][i];
         const float u = acc[tm][1][i];
-        Cs[r * LDC + c] = g / (1.0f + expf(-g)) * u;
+        Cs[r * LDC + c] = silu_mul(g, u);
       }
     __syncthreads();
     static_assert(OK == K_BF16, "gate/up output is bf16 here");
@@ -434,19 +434,41 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
     }
   } else {
     static_assert(OK == K_F32, "projection output is fp32 here");
+    // Staged through LDS in two passes of 256 columns, so that each lane
+    // stores 16 bytes and a wave stores one contiguous 1 KB row segment (the
+    // accumulator layout would give 4-byte stores, 4x the store instructions).
+    __syncthreads();  // all waves are done with the operand buffers
+    constexpr int LDC = 256 + 4;
+    float* Cs = reinterpret_cast<float*>(smem);
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm)
+    for (int half = 0; half < 2; ++half) {
+      if ((wn >> 2) == half) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = wm * 64 + tm * 32 + 8 * (i >> 2) + 4 * lhalf + (i & 3);
-        if (r >= job.rows_here) continue;
-        float* dst = reinterpret_cast<float*>(gemm_out_row<4>(p, job.row_begin + job.m0 + r));
+        for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < 2; ++tn) {
-          const int n = job.n0 + wn * 64 + tn * 32 + lrow;
-          if (n < N) dst[n] = acc[tm][tn][i];
+          for (int i = 0; i < 16; ++i) {
+            const int r = wm * 64 + tm * 32 + 8 * (i >> 2) + 4 * lhalf + (i & 3);
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn) Cs[r * LDC + (wn & 3) * 64 + tn * 32 + lrow] = acc[tm][tn][i];
+          }
+      }
+      __syncthreads();
+      for (int q = tid; q < BM * 64; q += THREADS) {
+        const int r = q >> 6;
+        const int c4 = (q & 63) * 4;
+        const int n = job.n0 + half * 256 + c4;
+        if (r < job.rows_here && n < N) {
+          const float* src = Cs + r * LDC + c4;
+          float* dst = reinterpret_cast<float*>(gemm_out_row<4>(p, job.row_begin + job.m0 + r));
+          if (n + 4 <= N) {
+            *reinterpret_cast<float4*>(dst + n) = float4{src[0], src[1], src[2], src[3]};
+          } else {
+            for (int i = 0; n + i < N; ++i) dst[n + i] = src[i];
+          }
         }
       }
+      __syncthreads();
+    }
   }
 }
 

@@ -117,7 +117,7 @@ __device__ __forceinline__ void decode_tile(const GemmLaunch& p, int b) {
             const float g = acc[m][j][i];
             const float u = acc[m][j + NT / 2][i];
             reinterpret_cast<uint16_t*>(gemm_out_row<2>(p, row))[n] =
-                f32_to_bf16(g / (1.0f + expf(-g)) * u);
+                f32_to_bf16(silu_mul(g, u));
           }
         }
       } else {

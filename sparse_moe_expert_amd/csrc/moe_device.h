@@ -23,6 +23,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// SiLU(g) * u of the SwiGLU epilogues, g / (1 + e^-g) * u, with the hardware
+// exponential and reciprocal (each within a few ulp in fp32: far below the
+// bf16 or e4m3 rounding of h that follows, and of the fp32 tolerance).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // Order-preserving map of an fp32 to uint32 (larger float -> larger uint).
 __device__ __forceinline__ uint32_t f32_order_key(float f) {
   uint32_t u = __float_as_uint(f);
