@@ -202,7 +202,9 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
     char* base = smem + (kt % NS) * STAGE;
     const int koff = (kt0 + kt) * 128;
 #pragma unroll
-    for (int i = 0; i < A_DMA; ++i) dma16(a_src[i] + koff, base + (i * WAVES + wave) * 1024);
+    for (int i = 0; i < A_DMA; ++i)
+      if ((i * WAVES + wave) * 8 < job.rows_here)  // rows past the tile's end are never read
+        dma16(a_src[i] + koff, base + (i * WAVES + wave) * 1024);
 #pragma unroll
     for (int i = 0; i < B_DMA; ++i)
       dma16(job.W + b_off[i] + koff, base + A_BYTES + (i * WAVES + wave) * 1024);
@@ -239,6 +241,10 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
       for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
   }
 
+  // which of this wave's row sub-tiles hold rows of the tile (wave-uniform)
+  const bool m_act[2] = {wm * 64 < job.rows_here, wm * 64 + 32 < job.rows_here};
+  const bool t_act[1] = {wm8 * 32 < job.rows_here};
+
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk) issue(s);
@@ -265,6 +271,9 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
       const float sbu = DUAL ? sb_cur[1] : sbg;
       const float sg[2] = {sa_cur[0] * sbg, sa_cur[1] * sbg};
       const float su[2] = {sa_cur[0] * sbu, sa_cur[1] * sbu};
+      // A wave whose 32 tokens all lie past the tile's last row (the ragged
+      // tail of an expert) skips the slice: its outputs are never stored.
+      if (!t_act[0]) continue;
       i32x8_t xf[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -289,21 +298,26 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
       }
       continue;
     }
+    // 32-row sub-tiles wholly past the tile's last row (the ragged tail of
+    // an expert) are skipped: their outputs are never stored
+    if (!m_act[0]) continue;
 #pragma unroll
     for (int s = 0; s < KE / 16; ++s) {
       const int ch = s * 2 + lhalf;
       bf16x8 a[2], b[2];
 #pragma unroll
       for (int tm = 0; tm < 2; ++tm)
-        a[tm] = *reinterpret_cast<const bf16x8*>(As + swz(wm * 64 + tm * 32 + lrow, ch));
+        if (m_act[tm]) a[tm] = *reinterpret_cast<const bf16x8*>(As + swz(wm * 64 + tm * 32 + lrow, ch));
 #pragma unroll
       for (int tn = 0; tn < 2; ++tn)
         b[tn] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * 64 + tn * 32 + lrow, ch));
 #pragma unroll
       for (int tm = 0; tm < 2; ++tm)
+        if (m_act[tm]) {
 #pragma unroll
-        for (int tn = 0; tn < 2; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
+          for (int tn = 0; tn < 2; ++tn)
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
+        }
     }
   }
 
