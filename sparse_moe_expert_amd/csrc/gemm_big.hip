@@ -134,6 +134,11 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
     a_src[i] = static_cast<const char*>(p.A) + src * rowb_a + lchunk * 16;
   }
   uint32_t b_off[B_DMA];
+  // projection: 8-row weight groups wholly past the last output column are
+  // not loaded (their rows would be clamped duplicates no stored output uses)
+  bool b_act[B_DMA];
+#pragma unroll
+  for (int i = 0; i < B_DMA; ++i) b_act[i] = job.n0 + (i * WAVES + wave) * 8 < N;
 #pragma unroll
   for (int i = 0; i < B_DMA; ++i) {
     const int r = (i * WAVES + wave) * 8 + rsub;
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
         dma16(a_src[i] + koff, base + (i * WAVES + wave) * 1024);
 #pragma unroll
     for (int i = 0; i < B_DMA; ++i)
-      dma16(job.W + b_off[i] + koff, base + A_BYTES + (i * WAVES + wave) * 1024);
+      if (DUAL || b_act[i]) dma16(job.W + b_off[i] + koff, base + A_BYTES + (i * WAVES + wave) * 1024);
     if constexpr (AK == K_FP8) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) sa_next[tt] = p.a_scale[sa_off[tt] + kt0 + kt];
@@ -241,9 +246,15 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
       for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
   }
 
-  // which of this wave's row sub-tiles hold rows of the tile (wave-uniform)
-  const bool m_act[2] = {wm * 64 < job.rows_here, wm * 64 + 32 < job.rows_here};
-  const bool t_act[1] = {wm8 * 32 < job.rows_here};
+  // whether this wave's row sub-tiles hold rows of the tile and (projection:
+  // the router's 256 experts fill half a 512-column tile) whether its weight
+  // rows give columns below N; work outside is never stored.  Wave-uniform.
+  // The gate/up tiles are not tested for columns: N = I is a multiple of
+  // the tile width in the workloads, and the test measured 2% slower there.
+  const bool n_act = DUAL || job.n0 + wn * 64 < N;
+  const bool m_act[2] = {n_act && wm * 64 < job.rows_here, n_act && wm * 64 + 32 < job.rows_here};
+  const bool n_act8 = DUAL || job.n0 + wn8 * 128 < N;
+  const bool t_act[1] = {n_act8 && wm8 * 32 < job.rows_here};
 
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
