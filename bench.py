@@ -244,7 +244,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the grouped-routing and block lines")
-    ap.add_argument("--cpu-tokens", type=int, default=768)
+    ap.add_argument("--cpu-tokens", type=int, default=1280)
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run one plain device-to-device copy of this many GiB "
                          "(calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
