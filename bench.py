@@ -130,12 +130,23 @@ def load_traffic(workload: str):
 
 
 def time_layer(lay, steps, warmup, timed_events=True):
+    """K plain layer forwards timed by the host clock between two device
+    synchronisations (the step time), then K more with HIP events recorded at
+    the stage boundaries on the layer's stream (the stage times; the events
+    themselves add ~25-50 us to a step, so they stay out of the first pass).
+    Returns (step ms, instrumented step ms, event step ms, stage ms, counts)."""
     import torch
     import sparse_moe_expert_amd as moe
     out = lay.empty_out()
     counts = torch.empty(lay.cfg.E, dtype=torch.int32, device="cuda")
     for _ in range(warmup):
         lay.forward(out=out, counts=counts)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        lay.forward(out=out, counts=counts)
+    torch.cuda.synchronize()
+    plain = (time.perf_counter() - t0) * 1e3 / steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
     for row in ev:          # torch creates the HIP event on its first record
         for e in row:
@@ -151,7 +162,7 @@ def time_layer(lay, steps, warmup, timed_events=True):
     stage = {n: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps
              for j, n in enumerate(names)}
     step_ev = sum(ev[i][0].elapsed_time(ev[i][6]) for i in range(steps)) / steps
-    return wall * 1e3 / steps, step_ev, stage, counts.cpu().numpy()
+    return plain, wall * 1e3 / steps, step_ev, stage, counts.cpu().numpy()
 
 
 def time_calls(fn, iters, warmup):
@@ -273,7 +284,7 @@ def main():
     torch.cuda.synchronize()
 
     log(f"bench: {args.warmup} warmup + {args.steps} timed steps")
-    ms, ms_ev, stage, counts = time_layer(lay, args.steps, args.warmup)
+    ms, ms_inst, ms_ev, stage, counts = time_layer(lay, args.steps, args.warmup)
     flops = cfg.flops()
     dtype = cfg.expert if cfg.expert != "f32" else "f32"
     res = {
@@ -293,6 +304,7 @@ def main():
                    "k": cfg.k, "I": cfg.I, "precision": dtype, "seed": 0},
         "tflops": round(flops / (ms / 1e3) / 1e12, 2),
         "frac_of_peak_mfma_whole_step": round(flops / (ms / 1e3) / 1e12 / PEAK_TFLOPS[dtype], 4),
+        "ms_per_step_instrumented": round(ms_inst, 4),
         "ms_per_step_events": round(ms_ev, 4),
         "stages_ms": {k: round(v, 4) for k, v in stage.items()},
         "rows_per_expert": {"max": int(counts.max()), "mean": float(counts.mean()),
@@ -309,7 +321,7 @@ def main():
         inp1 = generate(cfg1, weights=False)
         lay1 = _retarget(lay, cfg1, inp1)
         log(f"bench: decode T={cfg1.T}: {args.decode_steps} steps")
-        ms1, _, stage1, counts1 = time_layer(lay1, args.decode_steps, 5)
+        ms1, ms1_inst, _, stage1, counts1 = time_layer(lay1, args.decode_steps, 5)
         b1 = layer_bytes(cfg1, counts1)
         gbs = b1 / (ms1 / 1e3) / 1e9
         # the same layer as one cooperative launch
@@ -321,6 +333,7 @@ def main():
         gbf = b1 / (msf / 1e3) / 1e9
         res["decode_T256"] = {
             "workload": cfg1.name, "ms_per_step": round(ms1, 4),
+            "ms_per_step_instrumented": round(ms1_inst, 4),
             "fused_single_launch": {"ms_per_step": round(msf, 4), "hbm_GBps": round(gbf, 1),
                                     "frac_of_hbm_peak": round(gbf / PEAK_HBM_GBS, 4)},
             "tokens_per_s": round(cfg1.T / (ms1 / 1e3), 1),
