@@ -140,13 +140,17 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __
   }
 }
 
-__global__ __launch_bounds__(1024) void build_groups_kernel(
-    const int32_t* __restrict__ offsets, int T, int k, int E, int S, GroupDesc* __restrict__ groups,
-    int32_t* __restrict__ totals, int32_t* __restrict__ mtg_gu, int32_t* __restrict__ mtg_dn,
-    int bm_gu, int bm_dn, const char* w_gu, const float* s_gu,
-    const char* w_dn, const float* s_dn, const char* w_sh_gu, const float* s_sh_gu,
-    const char* w_sh_dn, const float* s_sh_dn, int H, int I, int esz, int fp8) {
-  __shared__ int sh[1024];
+// Tile table of the two grouped GEMMs, by one block of 1024 threads: group g
+// (routed experts, then the shared experts) gets its rows, its first m-tile
+// in each GEMM, its weight (and fp8 scale) pointers, and the m-tile -> group
+// lookup tables.  offsets: [E + 1] exclusive scan of the expert counts.
+__device__ void build_groups_body(const int32_t* offsets, int T, int k, int E, int S,
+                                  GroupDesc* __restrict__ groups, int32_t* __restrict__ totals,
+                                  int32_t* __restrict__ mtg_gu, int32_t* __restrict__ mtg_dn,
+                                  int bm_gu, int bm_dn, const char* w_gu, const float* s_gu,
+                                  const char* w_dn, const float* s_dn, const char* w_sh_gu,
+                                  const float* s_sh_gu, const char* w_sh_dn, const float* s_sh_dn,
+                                  int H, int I, int esz, int fp8, int* sh) {
   const int g = threadIdx.x;
   const int G = E + S;
   const int R = T * k;
@@ -189,6 +193,103 @@ __global__ __launch_bounds__(1024) void build_groups_kernel(
   }
 }
 
+__global__ __launch_bounds__(1024) void build_groups_kernel(
+    const int32_t* __restrict__ offsets, int T, int k, int E, int S, GroupDesc* __restrict__ groups,
+    int32_t* __restrict__ totals, int32_t* __restrict__ mtg_gu, int32_t* __restrict__ mtg_dn,
+    int bm_gu, int bm_dn, const char* w_gu, const float* s_gu,
+    const char* w_dn, const float* s_dn, const char* w_sh_gu, const float* s_sh_gu,
+    const char* w_sh_dn, const float* s_sh_dn, int H, int I, int esz, int fp8) {
+  __shared__ int sh[1024];
+  build_groups_body(offsets, T, k, E, S, groups, totals, mtg_gu, mtg_dn, bm_gu, bm_dn, w_gu, s_gu,
+                    w_dn, s_dn, w_sh_gu, s_sh_gu, w_sh_dn, s_sh_dn, H, I, esz, fp8, sh);
+}
+
+// The whole dispatch in one block of 16 waves when the pairs fit in 16 chunks
+// (T*k <= 16384, the decode regime): the pairs are cut into 16 chunks of a
+// multiple of 64, and wave w takes chunk w through the same three steps as
+// the separate kernels -- histogram, scan over chunks then experts, stable
+// scatter -- with the chunk table in LDS, then (if groups is set) the tile
+// table.  Same results, bit for bit; one launch instead of four.
+constexpr int kSmallChunks = 16;
+
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(
+    const int32_t* __restrict__ idx, int n, int E, int nchunks, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+    int T, int k, int S, GroupDesc* __restrict__ groups, int32_t* __restrict__ totals,
+    int32_t* __restrict__ mtg_gu, int32_t* __restrict__ mtg_dn, int bm_gu, int bm_dn,
+    const char* w_gu, const float* s_gu, const char* w_dn, const float* s_dn, const char* w_sh_gu,
+    const float* s_sh_gu, const char* w_sh_dn, const float* s_sh_dn, int H, int I, int esz,
+    int fp8) {
+  const int cs = max(64, (n + kSmallChunks * 64 - 1) / (kSmallChunks * 64) * 64);  // pairs per chunk
+  nchunks = (n + cs - 1) / cs;
+  __shared__ int32_t run[kSmallChunks][kMaxExperts];  // counts, then running positions
+  __shared__ int32_t s_off[kMaxExperts + 1];
+  __shared__ int sh[1024];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kSmallChunks * kMaxExperts; i += blockDim.x) (&run[0][0])[i] = 0;
+  __syncthreads();
+  // 1. histogram of chunk `wave`
+  if (wave < nchunks) {
+    const int f0 = wave * cs;
+    for (int r = 0; r < cs / 64; ++r) {
+      const int f = f0 + r * 64 + lane;
+      if (f < n) atomicAdd(&run[wave][idx[f]], 1);
+    }
+  }
+  __syncthreads();
+  // 2. per expert: running bases over chunks, then the exclusive scan over experts
+  const int e = threadIdx.x;
+  int tot_e = 0;
+  if (e < E)
+    for (int c = 0; c < nchunks; ++c) tot_e += run[c][e];
+  int total = 0;
+  const int excl = block_exclusive_scan(e < E ? tot_e : 0, sh, &total);
+  if (e < E) {
+    counts[e] = tot_e;
+    offsets[e] = excl;
+    s_off[e] = excl;
+    int acc = excl;
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = run[c][e];
+      run[c][e] = acc;
+      acc += v;
+    }
+  }
+  if (e == 0) {
+    offsets[E] = total;
+    s_off[E] = total;
+  }
+  __syncthreads();
+  // 3. stable scatter of chunk `wave` (as dispatch_scatter_kernel)
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int r = 0; r < cs / 64; ++r) {
+    const int f = wave * cs + r * 64 + lane;
+    const bool valid = (wave < nchunks) && (f < n);
+    const int ef = valid ? idx[f] : 0;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < kExpertBits; ++b) {
+      const bool bit = (ef >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & below);
+    const int base = valid ? run[wave][ef] : 0;
+    __syncthreads();  // every lane has read its base before any update
+    if (valid) {
+      const int pos = base + rank;
+      perm[pos] = f;
+      inv[f] = pos;
+      if (rank == 0) run[wave][ef] = base + __popcll(peers);
+    }
+    __syncthreads();
+  }
+  // 4. tile table
+  if (groups)
+    build_groups_body(s_off, T, k, E, S, groups, totals, mtg_gu, mtg_dn, bm_gu, bm_dn, w_gu, s_gu,
+                      w_dn, s_dn, w_sh_gu, s_sh_gu, w_sh_dn, s_sh_dn, H, I, esz, fp8, sh);
+}
+
 }  // namespace
 
 hipError_t launch_groups_only(const int32_t* offsets, int T, int k, int E, int S,
@@ -216,6 +317,15 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int T, int k, int E, int S,
                            const void* w_sh_dn, const float* s_sh_dn, int H, int I,
                            int expert_kind, hipStream_t st) {
   const int n = T * k;
+  if (nchunks <= kSmallChunks) {
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, st, topk_idx, n, E, nchunks,
+                       counts, offsets, perm, inv, T, k, S, groups, totals, mtg_gu, mtg_dn, gu.bm,
+                       dn.bm, static_cast<const char*>(w_gu), s_gu, static_cast<const char*>(w_dn),
+                       s_dn, static_cast<const char*>(w_sh_gu), s_sh_gu,
+                       static_cast<const char*>(w_sh_dn), s_sh_dn, H, I,
+                       static_cast<int>(kind_size(expert_kind)), expert_kind == K_FP8 ? 1 : 0);
+    return hipGetLastError();
+  }
   const int blocks = (nchunks + kWavesPerBlock - 1) / kWavesPerBlock;
   hipLaunchKernelGGL(dispatch_hist_kernel, dim3(blocks), dim3(256), 0, st, topk_idx, n, E,
                      nchunks, chunk_counts);
