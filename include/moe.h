@@ -168,7 +168,8 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx, int3
  *   y_sorted[p] = Wd_e h                                  fp32 [T*k, H]
  * and for every shared expert s and token t:
  *   y_shared[s, t] = Wd_s (SiLU(Wg_s x_t) * (Wu_s x_t))   fp32 [S, T, H]
- * fp32 accumulation; h is rounded to the activation type (bf16) between the
+ * fp32 accumulation (SiLU in fp32 with the hardware exponential and
+ * reciprocal); h is rounded to the activation type (bf16) between the
  * two GEMMs; y stays fp32 so that the layer output is rounded only once, in
  * moe_combine.  FP8: x and h are quantised per token per 128 channels to e4m3
  * with scale amax/448 (fp32, see moe_quantize_fp8) before their GEMM; weights

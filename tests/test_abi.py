@@ -90,8 +90,8 @@ def test_workspace_size_covers_buffers():
     n = moe.moe_workspace_size(c)
     R = 16384 * 8
     # h (bf16) + y_sorted and y_shared (fp32) + router logits (fp32, K split
-    # 4 ways at this T) + the normalised block input (bf16)
-    need = ((R + 16384) * 1536 * 2 + R * 5120 * 4 + 16384 * 5120 * 4 + 4 * 16384 * 256 * 4
+    # 2 ways at this T) + the normalised block input (bf16)
+    need = ((R + 16384) * 1536 * 2 + R * 5120 * 4 + 16384 * 5120 * 4 + 2 * 16384 * 256 * 4
             + 16384 * 5120 * 2)
     assert need <= n < need * 1.05
 
