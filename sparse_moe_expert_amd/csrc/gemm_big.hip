@@ -413,7 +413,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
             const float* src = Cs + r * LDC + c4;
             float* dst = reinterpret_cast<float*>(gemm_out_row<4>(p, job.row_begin + job.m0 + r));
             if (n + 4 <= N) {
-              *reinterpret_cast<float4*>(dst + n) = float4{src[0], src[1], src[2], src[3]};
+              __builtin_nontemporal_store(f32x4{src[0], src[1], src[2], src[3]},
+                                          reinterpret_cast<f32x4*>(dst + n));
             } else {
               for (int i = 0; n + i < N; ++i) dst[n + i] = src[i];
             }
