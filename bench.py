@@ -21,6 +21,10 @@ Extra objects in the line:
                routing (8 groups, 4 chosen) next to the plain router.
   block        the decoder block around the layer (RMSNorm, layer, residual
                add in the combine) and the RMSNorm kernel alone against HBM.
+  row_major_weights  the same layer with the expert weights row-major
+               (the timed line uses them packed into 16-row x 256-byte tiles
+               once at load time, moe_pack_expert_weights; --weights rows
+               times row-major weights instead).
   cpu_baseline the fp64 CPU oracle on the first tokens of the same workload.
 """
 from __future__ import annotations
@@ -40,7 +44,9 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE layer fwd tokens/s & TFLOP/s (T=16384); HBM GB/s at T=256; % roofline"
 GEMM_SRCS = [os.path.join(ROOT, "sparse_moe_expert_amd", "csrc", f)
-             for f in ("gemm.hip", "gemm_big.hip", "gemm_decode.hip", "gemm_sched.h")]
+             for f in ("gemm.hip", "gemm_big.hip", "gemm_decode.hip", "gemm_decode_device.h",
+                       "gemm_sched.h", "moe_device.h", "moe_internal.h")]
+EXPERT_KEYS = ("w_gate_up", "w_down", "w_sh_gate_up", "w_sh_down")
 
 
 def log(msg):
@@ -256,6 +262,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the grouped-routing and block lines")
     ap.add_argument("--cpu-tokens", type=int, default=1280)
+    ap.add_argument("--weights", choices=("tiled", "rows"), default="tiled",
+                    help="expert weight storage of the timed layer (default: packed tiles)")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run one plain device-to-device copy of this many GiB "
                          "(calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -280,7 +288,16 @@ def main():
     t0 = time.perf_counter()
     inp = generate(cfg)
     log(f"bench: generated in {time.perf_counter() - t0:.1f}s; uploading")
-    lay = DeviceLayer(cfg, inp)
+    lay_rows = DeviceLayer(cfg, inp)
+    tiled = args.weights == "tiled"
+    if tiled:
+        # load-time preparation, outside the timed region: the expert weights
+        # packed once into the tiled storage
+        from sparse_moe_expert_amd.device import pack_expert_weights
+        packed = {key: pack_expert_weights(lay_rows.t[key], cfg.expert) for key in EXPERT_KEYS}
+        lay = _view(lay_rows, cfg, expert_t=packed, tiled=True)
+    else:
+        lay = lay_rows
     torch.cuda.synchronize()
 
     log(f"bench: {args.warmup} warmup + {args.steps} timed steps")
@@ -301,7 +318,8 @@ def main():
         "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "S": cfg.S,
-                   "k": cfg.k, "I": cfg.I, "precision": dtype, "seed": 0},
+                   "k": cfg.k, "I": cfg.I, "precision": dtype, "seed": 0,
+                   "expert_weights": "tiled16x256B" if tiled else "row_major"},
         "tflops": round(flops / (ms / 1e3) / 1e12, 2),
         "frac_of_peak_mfma_whole_step": round(flops / (ms / 1e3) / 1e12 / PEAK_TFLOPS[dtype], 4),
         "ms_per_step_instrumented": round(ms_inst, 4),
@@ -319,7 +337,7 @@ def main():
         # every shape and weight distribution.
         cfg1 = config(1)
         inp1 = generate(cfg1, weights=False)
-        lay1 = _retarget(lay, cfg1, inp1)
+        lay1 = _view(lay, cfg1, inp1)
         log(f"bench: decode T={cfg1.T}: {args.decode_steps} steps")
         ms1, ms1_inst, _, stage1, counts1 = time_layer(lay1, args.decode_steps, 5)
         b1 = layer_bytes(cfg1, counts1)
@@ -343,6 +361,17 @@ def main():
             "stages_ms": {k: round(v, 4) for k, v in stage1.items()},
             "experts_touched": int((counts1 > 0).sum()),
         }
+        if tiled:
+            ms1r = time_layer(_view(lay_rows, cfg1, inp1), args.decode_steps, 5)[0]
+            g1r = b1 / (ms1r / 1e3) / 1e9
+            res["decode_T256"]["row_major_weights"] = {
+                "ms_per_step": round(ms1r, 4), "hbm_GBps": round(g1r, 1),
+                "frac_of_hbm_peak": round(g1r / PEAK_HBM_GBS, 4)}
+
+    if tiled:
+        msr = time_layer(lay_rows, args.steps, args.warmup)[0]
+        res["row_major_weights"] = {"ms_per_step": round(msr, 4),
+                                    "tokens_per_s": round(cfg.T / (msr / 1e3), 1)}
 
     if not args.no_extras and args.config == 2:
         log("bench: grouped routing and block forward")
@@ -367,9 +396,10 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def _retarget(lay, cfg1, inp1):
-    """A DeviceLayer view with another token batch and router, reusing the
-    resident expert weights of `lay` (same shapes)."""
+def _view(lay, cfg1, inp1=None, expert_t=None, tiled=None):
+    """A DeviceLayer view of `lay` (same shapes) with another token batch and
+    router (inp1) and/or other expert weight tensors (expert_t, stored as
+    `tiled` says; default: as in `lay`).  Everything else is shared."""
     import torch
 
     from sparse_moe_expert_amd import _lib
@@ -380,16 +410,25 @@ def _retarget(lay, cfg1, inp1):
 
     v = View()
     v.cfg = cfg1
+    v.tiled = lay.tiled if tiled is None else tiled
     v.ccfg = _lib.make_config(cfg1.T, cfg1.H, cfg1.E, cfg1.S, cfg1.k, cfg1.I, cfg1.Is,
-                              act=cfg1.act, expert=cfg1.expert)
+                              act=cfg1.act, expert=cfg1.expert,
+                              norm_topk_prob=cfg1.norm_topk_prob,
+                              routed_scaling_factor=cfg1.routed_scaling_factor,
+                              n_group=cfg1.n_group, topk_group=cfg1.topk_group, tiled=v.tiled)
     t = dict(lay.t)
-    t["x"] = to_device(inp1["x"], cfg1.act)
-    t["w_router"] = to_device(inp1["w_router"], cfg1.act)
-    t["bias"] = to_device(inp1["bias"], "f32")
+    if inp1 is not None:
+        t["x"] = to_device(inp1["x"], cfg1.act)
+        t["w_router"] = to_device(inp1["w_router"], cfg1.act)
+        t["bias"] = to_device(inp1["bias"], "f32")
+    if expert_t is not None:
+        t.update(expert_t)
     v.t = t
     v.weights = _lib.make_weights(
         w_router=t["w_router"], router_bias=t["bias"], w_gate_up=t["w_gate_up"],
-        w_down=t["w_down"], w_sh_gate_up=t["w_sh_gate_up"], w_sh_down=t["w_sh_down"])
+        w_down=t["w_down"], s_gate_up=t.get("s_gate_up"), s_down=t.get("s_down"),
+        w_sh_gate_up=t["w_sh_gate_up"], w_sh_down=t["w_sh_down"],
+        s_sh_gate_up=t.get("s_sh_gate_up"), s_sh_down=t.get("s_sh_down"))
     v.ws_bytes = _lib.moe_workspace_size(v.ccfg)
     v.workspace = torch.empty(v.ws_bytes, dtype=torch.uint8, device="cuda")
     v.act_dtype = lay.act_dtype

@@ -62,6 +62,14 @@ typedef enum {
   MOE_FP8_E4M3 = 2  /* OCP FP8 E4M3 (bias 7, max 448, no inf), gfx950 native */
 } moe_dtype_t;
 
+/* Storage of the expert weight matrices (w_gate_up, w_down, w_sh_gate_up,
+ * w_sh_down; never the router weight).  Both hold the same values, only the
+ * byte order differs; see moe_pack_expert_weights. */
+typedef enum {
+  MOE_LAYOUT_ROWS = 0,  /* row-major, as the shapes below state              */
+  MOE_LAYOUT_TILED = 1  /* 16-row x 256-byte tiles (moe_pack_expert_weights) */
+} moe_layout_t;
+
 /* Layer shape and options; field names follow the model config fields
  * [AA «核心架构参数一览»; D1 «MoE 路由与专家相关字段»]. */
 typedef struct moe_config {
@@ -82,6 +90,10 @@ typedef struct moe_config {
   int32_t topk_group;   /* groups a token may choose from, 1..n_group
                            (ignored without grouping); k <= topk_group *
                            E / n_group                                       */
+  int32_t expert_layout; /* moe_layout_t of the expert weights; TILED needs
+                           H and I times the expert element size to be
+                           multiples of 256 bytes (FP8: H, I multiples of
+                           256), else MOE_ERR_UNSUPPORTED                    */
 } moe_config_t;
 
 /* Weights of one layer (device pointers).
@@ -110,6 +122,28 @@ typedef struct moe_weights {
   const float* s_sh_gate_up;
   const float* s_sh_down;
 } moe_weights_t;
+
+/* Expert weight storage [D1 «并行策略字段»: gate_up_proj and down_proj as
+ * stacked per-expert matrices].  No arithmetic: copies `count` row-major
+ * [rows, cols] matrices of `dtype` elements from src into dst in the
+ * MOE_LAYOUT_TILED order.  Each matrix is cut into 16-row x 256-byte tiles
+ * (4 KB); tiles are stored row group by row group, and along the row inside
+ * a row group; inside a tile each of its 16 rows keeps its 256 bytes
+ * contiguous.  So byte b of row r of matrix m lands at
+ *   m*rows*rb + (r/16)*16*rb + (b/256)*4096 + (r%16)*256 + b%256,
+ * rb = cols * element size.  Matrix m starts at the same byte offset in
+ * both layouts, so per-expert pointers and the FP8 block scales are
+ * unchanged.  Use: pack w_gate_up with (E, 2I, H), w_down with (E, H, I),
+ * and the shared ones with S, then set expert_layout = MOE_LAYOUT_TILED.
+ * The GEMMs then read each 16-row weight tile as contiguous 4 KB runs.
+ * src and dst: device, 16-byte aligned, not overlapping, count*rows*rb
+ * bytes each.  count >= 0 (0: no-op), rows > 0, cols > 0 and dtype a
+ * moe_dtype_t, else MOE_ERR_INVALID_ARG (also for null, misaligned or
+ * overlapping buffers); rows not a multiple of 16 or rb not a multiple of
+ * 256: MOE_ERR_UNSUPPORTED.  Enqueued on `stream`; dst is complete when the
+ * stream reaches that point. */
+moe_status_t moe_pack_expert_weights(const void* src, void* dst, int64_t count, int32_t rows,
+                                     int32_t cols, int32_t dtype, moe_stream_t stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* moe_status_string(moe_status_t status);

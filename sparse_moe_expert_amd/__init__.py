@@ -18,7 +18,8 @@ _BINDING = (
     "moe_expert_down", "moe_expert_gate_up", "moe_grouped_ffn", "moe_layer_forward",
     "moe_layer_forward_timed", "moe_rmsnorm", "moe_block_forward", "moe_layer_forward_fused",
     "moe_quantize_fp8", "moe_route", "moe_weights_t", "moe_workspace_size", "status_string",
-    "version", "last_error_detail",
+    "version", "last_error_detail", "moe_pack_expert_weights", "MOE_LAYOUT_ROWS",
+    "MOE_LAYOUT_TILED",
 )
 
 __all__ = list(_BINDING)

@@ -16,12 +16,14 @@ LIB_PATH = os.environ.get("MOE_LIB", os.path.join(_PKG, "libmoe.so"))
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 
 # every entry point of include/moe.h
 EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_version", "moe_workspace_size", "moe_route",
            "moe_dispatch", "moe_grouped_ffn", "moe_expert_gate_up", "moe_expert_down",
            "moe_combine", "moe_quantize_fp8", "moe_layer_forward", "moe_layer_forward_timed",
-           "moe_rmsnorm", "moe_block_forward", "moe_layer_forward_fused")
+           "moe_rmsnorm", "moe_block_forward", "moe_layer_forward_fused",
+           "moe_pack_expert_weights")
 
 
 class MoEError(RuntimeError):
@@ -38,7 +40,7 @@ class moe_config_t(ctypes.Structure):
                 ("I_shared", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
                 ("routed_scaling_factor", ctypes.c_float), ("act_dtype", ctypes.c_int32),
                 ("expert_dtype", ctypes.c_int32), ("n_group", ctypes.c_int32),
-                ("topk_group", ctypes.c_int32)]
+                ("topk_group", ctypes.c_int32), ("expert_layout", ctypes.c_int32)]
 
 
 class moe_weights_t(ctypes.Structure):
@@ -72,6 +74,8 @@ def _load():
         "moe_expert_down": (ctypes.c_int, [CP, WP, P, P, P, SZ, P]),
         "moe_combine": (ctypes.c_int, [CP, P, P, P, I32P, P, P]),
         "moe_quantize_fp8": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32, P, P, P]),
+        "moe_pack_expert_weights": (ctypes.c_int, [P, P, ctypes.c_int64, ctypes.c_int32,
+                                                   ctypes.c_int32, ctypes.c_int32, P]),
         "moe_layer_forward": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P, SZ, P]),
         "moe_layer_forward_timed": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P, SZ, P,
                                                    ctypes.POINTER(ctypes.c_void_p)]),
@@ -104,10 +108,11 @@ def version() -> str:
 
 def make_config(T, H, E, S, k, I, I_shared=None, act="bf16", expert="bf16",
                 norm_topk_prob=True, routed_scaling_factor=1.0, n_group=1,
-                topk_group=1) -> moe_config_t:
+                topk_group=1, tiled=False) -> moe_config_t:
     return moe_config_t(T, H, E, S, k, I, I if I_shared is None else I_shared,
                         1 if norm_topk_prob else 0, float(routed_scaling_factor),
-                        DTYPES[act], DTYPES[expert], int(n_group), int(topk_group))
+                        DTYPES[act], DTYPES[expert], int(n_group), int(topk_group),
+                        MOE_LAYOUT_TILED if tiled else MOE_LAYOUT_ROWS)
 
 
 def _ptr(t) -> int | None:
@@ -190,6 +195,13 @@ def moe_combine(cfg, y_sorted, y_shared, topk_w, inv, out, stream=None):
 def moe_quantize_fp8(x, rows, cols, q, scales, stream=None):
     _check(LIB.moe_quantize_fp8(_ptr(x), rows, cols, _ptr(q), _ptr(scales), _stream(stream)),
            "moe_quantize_fp8")
+
+
+def moe_pack_expert_weights(src, dst, count, rows, cols, dtype, stream=None):
+    """dtype: "f32" | "bf16" | "fp8" (or a moe_dtype_t value)."""
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    _check(LIB.moe_pack_expert_weights(_ptr(src), _ptr(dst), int(count), int(rows), int(cols), dt,
+                                       _stream(stream)), "moe_pack_expert_weights")
 
 
 def moe_layer_forward(cfg, weights, x, out, opt_counts=None, opt_tie_counts=None, workspace=None,

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
     const int c = q & 7;
     const int sb = r / BN;
     const int n = min(n0 + (r - sb * BN), p.N - 1);
-    b_src[i] = W + static_cast<long long>(sb * p.N + n) * row_bytes_b + c * 16;
+    b_src[i] = W + w_tile_row_off(p.w_tiled, sb * p.N + n, row_bytes_b) + c * 16;
     b_lds[i] = C::A_BYTES + swz(r, c);
   }
   // FP8: row scales of A (one per row and 128-K block) and the W block scales
@@ -226,11 +226,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
   float ras = 0.f;
   auto gload = [&](int kt) {
     const int koff = kt * 128;
+    // a K-stage is 128 bytes, so it never straddles a 256-byte tile column
+    const long long koff_b = w_tile_k_off(p.w_tiled, koff);
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i)
       if (a_on[i]) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + koff);
 #pragma unroll
-    for (int i = 0; i < C::B_LOADS; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + koff);
+    for (int i = 0; i < C::B_LOADS; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + koff_b);
     if constexpr (AK == K_FP8) {
       if (tid < BM) ras = a_scale_src[kt];
     }

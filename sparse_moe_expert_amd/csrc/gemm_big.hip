@@ -152,7 +152,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
     } else {
       wr = min(job.n0 + r, N - 1);
     }
-    b_off[i] = static_cast<uint32_t>(wr * rowb_b + lchunk * 16);
+    b_off[i] = static_cast<uint32_t>(w_tile_row_off(p.w_tiled, wr, rowb_b) + lchunk * 16);
   }
 
   // wave (wm, wn): rows [wm*64, +64) x B-tile rows [wn*64, +64)
@@ -206,13 +206,15 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
   auto issue = [&](int kt) {
     char* base = smem + (kt % NS) * STAGE;
     const int koff = (kt0 + kt) * 128;
+    // a K-slice is 128 bytes, so it never straddles a 256-byte tile column
+    const int koff_b = static_cast<int>(w_tile_k_off(p.w_tiled, koff));
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i)
       if ((i * WAVES + wave) * 8 < job.rows_here)  // rows past the tile's end are never read
         dma16(a_src[i] + koff, base + (i * WAVES + wave) * 1024);
 #pragma unroll
     for (int i = 0; i < B_DMA; ++i)
-      if (DUAL || b_act[i]) dma16(job.W + b_off[i] + koff, base + A_BYTES + (i * WAVES + wave) * 1024);
+      if (DUAL || b_act[i]) dma16(job.W + b_off[i] + koff_b, base + A_BYTES + (i * WAVES + wave) * 1024);
     if constexpr (AK == K_FP8) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) sa_next[tt] = p.a_scale[sa_off[tt] + kt0 + kt];

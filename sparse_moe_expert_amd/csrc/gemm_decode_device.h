@@ -49,7 +49,7 @@ __device__ __forceinline__ void decode_tile(const GemmLaunch& p, int b) {
     } else {
       wr = min(wn0 + t * 16 + lrow, N - 1);
     }
-    bptr[t] = job.W + wr * rowb_b + lgrp * 16;
+    bptr[t] = job.W + w_tile_row_off(p.w_tiled, wr, rowb_b) + lgrp * 16;
   }
   const char* aptr[MT];
 #pragma unroll
@@ -59,12 +59,15 @@ __device__ __forceinline__ void decode_tile(const GemmLaunch& p, int b) {
     aptr[m] = static_cast<const char*>(p.A) + src * rowb_a + lgrp * 16;
   }
 
+  // a 128-wide K-block of bf16 is one 256-byte tile column of the tiled layout
+  const int kb_stride_b = p.w_tiled ? kTileRows * kTileBytes : 256;
   auto load = [&](Regs<MT, NT>& R, int kb) {
     const int off = kb * 256;
+    const int off_b = kb * kb_stride_b;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) R.b[t][s] = *reinterpret_cast<const uint4*>(bptr[t] + off + s * 64);
+      for (int s = 0; s < 4; ++s) R.b[t][s] = *reinterpret_cast<const uint4*>(bptr[t] + off_b + s * 64);
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll

@@ -45,6 +45,15 @@ moe_status_t check_config(const moe_config_t* c) {
   // expert storage must match the activation type (FP8 experts take bf16 x)
   if (c->act_dtype == MOE_F32 && c->expert_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
   if (c->act_dtype == MOE_BF16 && c->expert_dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
+  // tiled expert weights: whole 256-byte tile columns along both K (H and I);
+  // the row counts 2I and H are multiples of 128 already
+  if (c->expert_layout != MOE_LAYOUT_ROWS && c->expert_layout != MOE_LAYOUT_TILED)
+    return MOE_ERR_INVALID_ARG;
+  if (c->expert_layout == MOE_LAYOUT_TILED) {
+    const long long esz = c->expert_dtype == MOE_F32 ? 4 : c->expert_dtype == MOE_BF16 ? 2 : 1;
+    if ((c->H * esz) % kTileBytes != 0 || (c->I * esz) % kTileBytes != 0)
+      return MOE_ERR_UNSUPPORTED;
+  }
   // index arithmetic stays in int32 for rows and in int64 for element offsets
   const long long R = static_cast<long long>(c->T) * c->k;
   const long long rows_all = R + static_cast<long long>(c->S) * c->T;
@@ -178,6 +187,7 @@ GemmLaunch gate_up_launch(const moe_config_t& c, const Layout& L, const void* x,
   g.c_split = LLONG_MAX;
   g.ldc = c.I;
   g.c_scale = fp8 ? at<float>(ws, L.hs) : nullptr;
+  g.w_tiled = c.expert_layout == MOE_LAYOUT_TILED;
   return g;
 }
 
@@ -291,6 +301,7 @@ GemmLaunch down_launch(const moe_config_t& c, const Layout& L, void* y_sorted, v
   g.C2 = y_shared;
   g.c_split = static_cast<long long>(c.T) * c.k;
   g.ldc = c.H;
+  g.w_tiled = c.expert_layout == MOE_LAYOUT_TILED;
   return g;
 }
 
@@ -525,6 +536,24 @@ moe_status_t moe_quantize_fp8(const void* x_bf16, int32_t rows, int32_t cols, ui
   clear_stale_error();
   return hip_status(launch_quant_rows_fp8(static_cast<const uint16_t*>(x_bf16), rows, cols, q,
                                           scales, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_pack_expert_weights(const void* src, void* dst, int64_t count, int32_t rows,
+                                     int32_t cols, int32_t dtype, moe_stream_t stream) {
+  if (count < 0 || rows <= 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  const long long rb = static_cast<long long>(cols) * (dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 2 : 1);
+  if (rows % kTileRows != 0 || rb % kTileBytes != 0) return MOE_ERR_UNSUPPORTED;
+  if (count == 0) return MOE_OK;
+  const long long matrix = static_cast<long long>(rows) * rb;
+  if (count > LLONG_MAX / matrix) return MOE_ERR_INVALID_ARG;
+  const long long bytes = count * matrix;
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return MOE_ERR_INVALID_ARG;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + static_cast<uintptr_t>(bytes) && b < a + static_cast<uintptr_t>(bytes))
+    return MOE_ERR_INVALID_ARG;  // overlapping
+  clear_stale_error();
+  return hip_status(launch_pack_tiles(src, dst, count, rows, rb, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,

@@ -74,6 +74,22 @@ Layout make_layout(const moe_config_t& c);
 
 inline size_t kind_size(int kind) { return kind == K_F32 ? 4 : kind == K_BF16 ? 2 : 1; }
 
+// Tiled weight storage: a row-major [rows, K] matrix (rows a multiple of 16,
+// K * element size a multiple of 256 bytes) cut into 16-row x 256-byte tiles
+// of 4 KB.  Tiles are stored row group by row group, and along K inside a
+// row group; inside a tile each row's 256 bytes are contiguous.  The byte
+// offset of (row, byte b of the row) splits into a row part and a K part,
+// which the kernels add separately; b % 256 carries into no other field.
+constexpr int kTileRows = 16;
+constexpr int kTileBytes = 256;
+__host__ __device__ inline long long w_tile_row_off(int tiled, int row, long long row_bytes) {
+  return tiled ? static_cast<long long>(row >> 4) * (row_bytes * kTileRows) + (row & 15) * kTileBytes
+               : static_cast<long long>(row) * row_bytes;
+}
+__host__ __device__ inline long long w_tile_k_off(int tiled, long long kbyte) {
+  return tiled ? (kbyte >> 8) * (kTileRows * kTileBytes) + (kbyte & 255) : kbyte;
+}
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  All take the caller's stream.
 
@@ -108,6 +124,9 @@ struct GemmLaunch {
   // [y * K / k_splits, (y + 1) * K / k_splits) into C + y * c_split_stride
   int k_splits;            // 0 or 1: no split
   long long c_split_stride;  // elements
+  // expert weights (groups' w_gu / w_dn) stored as 16-row x 256-byte tiles
+  // (w_tile_row_off / w_tile_k_off); the router's b_single is always row-major
+  int w_tiled;
 };
 
 hipError_t launch_gemm(int a_kind, int out_kind, TileShape ts, const GemmLaunch& g,
@@ -163,6 +182,9 @@ bool fused_decode_supported(TileShape gu, TileShape dn);
 hipError_t launch_fused_decode(const FusedArgs& a, hipStream_t st);
 
 // RMSNorm rows of [T, H] (act kind F32 or BF16), fp32 math, one rounding.
+// pack.hip: `count` row-major [rows, row_bytes] matrices -> tiled storage
+hipError_t launch_pack_tiles(const void* src, void* dst, long long count, int rows,
+                             long long row_bytes, hipStream_t st);
 hipError_t launch_rmsnorm(int act_kind, const void* h, const void* gamma, float eps, void* out,
                           int T, int H, hipStream_t st);
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t st);

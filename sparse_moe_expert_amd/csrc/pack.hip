@@ -1,0 +1,51 @@
+// Expert weights rearranged into the tiled storage of moe_internal.h
+// (w_tile_row_off / w_tile_k_off): 16-row x 256-byte tiles, 4 KB each.
+//
+// A pure byte permutation, done once when the weights are loaded.  With it
+// each 16-row weight tile that a GEMM wave streams is one contiguous 4 KB
+// run per 256 bytes of K, instead of 16 row pieces 2*K bytes apart.
+//
+// One thread moves one 16-byte chunk.  Threads walk the output in order, so
+// the stores are contiguous; 16 neighbouring threads read one row's 256
+// contiguous bytes.  Grid-stride loop over all chunks of all matrices.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void pack_tiles_kernel(const uint4* __restrict__ src,
+                                                         uint4* __restrict__ dst,
+                                                         long long total_chunks,
+                                                         long long matrix_chunks,
+                                                         long long row_bytes) {
+  const long long tiles_per_group = row_bytes / kTileBytes;
+  for (long long q = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+       q < total_chunks; q += static_cast<long long>(gridDim.x) * blockDim.x) {
+    const long long m = q / matrix_chunks;
+    const long long o = (q - m * matrix_chunks) * 16;  // byte offset in the tiled matrix
+    const long long tile = o / (kTileRows * kTileBytes);
+    const int in_tile = static_cast<int>(o - tile * (kTileRows * kTileBytes));
+    const long long group = tile / tiles_per_group;
+    const long long tcol = tile - group * tiles_per_group;
+    const long long row = group * kTileRows + in_tile / kTileBytes;
+    const long long byte = tcol * kTileBytes + in_tile % kTileBytes;
+    dst[q] = src[(m * matrix_chunks * 16 + row * row_bytes + byte) / 16];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack_tiles(const void* src, void* dst, long long count, int rows,
+                             long long row_bytes, hipStream_t st) {
+  const long long matrix_chunks = static_cast<long long>(rows) * row_bytes / 16;
+  const long long total = count * matrix_chunks;
+  if (total <= 0) return hipSuccess;
+  const long long want = (total + 255) / 256;
+  const unsigned grid = static_cast<unsigned>(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(pack_tiles_kernel, dim3(grid), dim3(256), 0, st,
+                     static_cast<const uint4*>(src), static_cast<uint4*>(dst), total,
+                     matrix_chunks, row_bytes);
+  return hipGetLastError();
+}
+
+}  // namespace moe

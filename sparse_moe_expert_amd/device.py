@@ -38,16 +38,32 @@ def to_host_bits(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
-class DeviceLayer:
-    """All inputs of one layer resident in device memory, plus a workspace."""
+def pack_expert_weights(w: torch.Tensor, kind: str, stream=None) -> torch.Tensor:
+    """[n, rows, cols] row-major device tensor -> a new tensor of the same
+    shape and dtype holding the MOE_LAYOUT_TILED byte order (the library's
+    moe_pack_expert_weights; the shape no longer indexes the elements)."""
+    w = w.contiguous()
+    out = torch.empty_like(w)
+    n, rows, cols = w.shape
+    _lib.moe_pack_expert_weights(w, out, n, rows, cols, kind, stream)
+    return out
 
-    def __init__(self, cfg, inp: dict, device: str = "cuda"):
+
+class DeviceLayer:
+    """All inputs of one layer resident in device memory, plus a workspace.
+
+    tiled=True stores the expert weights in MOE_LAYOUT_TILED order: they are
+    uploaded row-major, packed on the device once, and the row-major copies
+    are dropped."""
+
+    def __init__(self, cfg, inp: dict, device: str = "cuda", tiled: bool = False):
         self.cfg = cfg
         self.device = device
+        self.tiled = tiled
         self.ccfg = make_config(cfg.T, cfg.H, cfg.E, cfg.S, cfg.k, cfg.I, cfg.Is, act=cfg.act,
                                 expert=cfg.expert, norm_topk_prob=cfg.norm_topk_prob,
                                 routed_scaling_factor=cfg.routed_scaling_factor,
-                                n_group=cfg.n_group, topk_group=cfg.topk_group)
+                                n_group=cfg.n_group, topk_group=cfg.topk_group, tiled=tiled)
         ek = cfg.expert
         t = {
             "x": to_device(inp["x"], cfg.act, device),
@@ -61,6 +77,9 @@ class DeviceLayer:
         if ek == "fp8":
             for key in ("s_gate_up", "s_down", "s_sh_gate_up", "s_sh_down"):
                 t[key] = to_device(inp[key], "f32", device)
+        if tiled:
+            for key in ("w_gate_up", "w_down", "w_sh_gate_up", "w_sh_down"):
+                t[key] = pack_expert_weights(t[key], ek)
         self.t = t
         self.weights = make_weights(
             w_router=t["w_router"], router_bias=t["bias"], w_gate_up=t["w_gate_up"],

@@ -33,15 +33,25 @@ def test_exports_match_header():
         assert getattr(moe.LIB, name) is not None
 
 
+def test_package_reexports_every_wrapper():
+    """Every C entry point with a Python wrapper in the binding is reachable
+    from the package itself."""
+    import sparse_moe_expert_amd as pkg
+    for name in moe.EXPORTS:
+        if hasattr(moe, name):
+            assert name in pkg.__all__, name
+            assert getattr(pkg, name) is getattr(moe, name)
+
+
 def test_struct_layout_matches_c():
     src = r"""
 #include <stdio.h>
 #include <stddef.h>
 #include "moe.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(moe_config_t), offsetof(moe_config_t, routed_scaling_factor),
-         offsetof(moe_config_t, expert_dtype), sizeof(moe_weights_t),
-         offsetof(moe_weights_t, s_gate_up), offsetof(moe_weights_t, s_sh_down));
+  printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(moe_config_t), offsetof(moe_config_t, routed_scaling_factor),
+         offsetof(moe_config_t, expert_dtype), offsetof(moe_config_t, expert_layout),
+         sizeof(moe_weights_t), offsetof(moe_weights_t, s_gate_up), offsetof(moe_weights_t, s_sh_down));
   return 0;
 }
 """
@@ -54,7 +64,8 @@ int main(void) {
                                             check=True).stdout.split()))
     C, W = moe.moe_config_t, moe.moe_weights_t
     assert vals == [ctypes.sizeof(C), C.routed_scaling_factor.offset, C.expert_dtype.offset,
-                    ctypes.sizeof(W), W.s_gate_up.offset, W.s_sh_down.offset]
+                    C.expert_layout.offset, ctypes.sizeof(W), W.s_gate_up.offset,
+                    W.s_sh_down.offset]
 
 
 def test_status_strings_and_version():
@@ -79,6 +90,11 @@ def cfg(**kw):
     (dict(k=17, E=64), False), (dict(H=500), False), (dict(I=100), False), (dict(S=5), False),
     (dict(I_shared=256), False), (dict(act="f32", expert="bf16"), False),
     (dict(act="bf16", expert="f32"), False), (dict(T=-1), False),
+    # tiled expert weights need whole 256-byte tile columns along H and I
+    (dict(tiled=True), True), (dict(act="bf16", expert="bf16", tiled=True), True),
+    (dict(act="bf16", expert="fp8", tiled=True), False),         # I = 128 fp8 = 128 bytes
+    (dict(act="bf16", expert="fp8", I=256, tiled=True), True),
+    (dict(act="bf16", expert="fp8", H=640, I=256, tiled=True), False),
 ])
 def test_workspace_size_validates(kw, ok):
     n = moe.moe_workspace_size(cfg(**kw))
@@ -191,3 +207,29 @@ def test_python_binding_raises_moe_error():
     with pytest.raises(moe.MoEError) as ei:
         moe.moe_combine(c, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+def test_bad_layout_value_rejected():
+    c = cfg()
+    c.expert_layout = 2
+    assert moe.moe_workspace_size(c) == 0
+
+
+def test_pack_validation():
+    P = "moe_pack_expert_weights"
+    A, B = FAKE, FAKE + (1 << 24)   # far enough apart not to overlap below
+    assert call(P, A, B, 0, 16, 128, moe.MOE_BF16, None) == moe.MOE_OK    # count 0: no-op
+    assert call(P, A, B, -1, 16, 128, moe.MOE_BF16, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(P, A, B, 1, 0, 128, moe.MOE_BF16, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(P, A, B, 1, 16, 0, moe.MOE_BF16, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(P, A, B, 1, 16, 128, 7, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(P, A, B, 1, 24, 128, moe.MOE_BF16, None) == moe.MOE_ERR_UNSUPPORTED  # rows % 16
+    assert call(P, A, B, 1, 16, 64, moe.MOE_BF16, None) == moe.MOE_ERR_UNSUPPORTED   # 128-byte rows
+    assert call(P, A, B, 1, 16, 128, moe.MOE_FP8_E4M3, None) == moe.MOE_ERR_UNSUPPORTED
+    assert call(P, None, B, 1, 16, 128, moe.MOE_BF16, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(P, A, None, 1, 16, 128, moe.MOE_BF16, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(P, A + 8, B, 1, 16, 128, moe.MOE_BF16, None) == moe.MOE_ERR_INVALID_ARG
+    # overlapping source and destination (4 KB matrix, 2 KB apart)
+    assert call(P, A, A + 2048, 1, 16, 128, moe.MOE_BF16, None) == moe.MOE_ERR_INVALID_ARG
+    # byte count overflowing int64
+    assert call(P, A, B, 1 << 62, 16, 128, moe.MOE_BF16, None) == moe.MOE_ERR_INVALID_ARG
