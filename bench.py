@@ -260,7 +260,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the T=256 line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the grouped-routing and block lines")
+                    help="skip the grouped-routing, block and row-major-weights lines")
     ap.add_argument("--cpu-tokens", type=int, default=1280)
     ap.add_argument("--weights", choices=("tiled", "rows"), default="tiled",
                     help="expert weight storage of the timed layer (default: packed tiles)")
@@ -361,14 +361,14 @@ def main():
             "stages_ms": {k: round(v, 4) for k, v in stage1.items()},
             "experts_touched": int((counts1 > 0).sum()),
         }
-        if tiled:
+        if tiled and not args.no_extras:
             ms1r = time_layer(_view(lay_rows, cfg1, inp1), args.decode_steps, 5)[0]
             g1r = b1 / (ms1r / 1e3) / 1e9
             res["decode_T256"]["row_major_weights"] = {
                 "ms_per_step": round(ms1r, 4), "hbm_GBps": round(g1r, 1),
                 "frac_of_hbm_peak": round(g1r / PEAK_HBM_GBS, 4)}
 
-    if tiled:
+    if tiled and not args.no_extras:
         msr = time_layer(lay_rows, args.steps, args.warmup)[0]
         res["row_major_weights"] = {"ms_per_step": round(msr, 4),
                                     "tokens_per_s": round(cfg.T / (msr / 1e3), 1)}
