@@ -109,10 +109,22 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   // ---------------------------------------------------------------- B
   {
     __shared__ float cbuf[4][kMaxExperts];
-    for (long long t = gwave; t < a.T; t += nwaves)
-      router_topk_token(a.logits, a.splits, a.bias, a.T, a.E, a.k, a.n_group, a.topk_group,
-                        a.norm, a.rsf, a.idx, a.tw, a.ties, static_cast<int>(t), lane,
-                        cbuf[wave]);
+    const int kper = router_keys_per_lane(a.E);
+    for (long long t = gwave; t < a.T; t += nwaves) {
+      const int ti = static_cast<int>(t);
+      if (kper == 1)
+        router_topk_token<1>(a.logits, a.splits, a.bias, a.T, a.E, a.k, a.n_group, a.topk_group,
+                             a.norm, a.rsf, a.idx, a.tw, a.ties, ti, lane, cbuf[wave]);
+      else if (kper == 2)
+        router_topk_token<2>(a.logits, a.splits, a.bias, a.T, a.E, a.k, a.n_group, a.topk_group,
+                             a.norm, a.rsf, a.idx, a.tw, a.ties, ti, lane, cbuf[wave]);
+      else if (kper == 4)
+        router_topk_token<4>(a.logits, a.splits, a.bias, a.T, a.E, a.k, a.n_group, a.topk_group,
+                             a.norm, a.rsf, a.idx, a.tw, a.ties, ti, lane, cbuf[wave]);
+      else
+        router_topk_token<8>(a.logits, a.splits, a.bias, a.T, a.E, a.k, a.n_group, a.topk_group,
+                             a.norm, a.rsf, a.idx, a.tw, a.ties, ti, lane, cbuf[wave]);
+    }
   }
   grid.sync();
 

@@ -28,6 +28,7 @@ namespace {
 
 constexpr int kWaves = 4;  // waves (tokens) per block
 
+template <int KPER>
 __global__ __launch_bounds__(64 * kWaves) void router_topk_kernel(const float* __restrict__ logits,
                                                           int splits,
                                                           const float* __restrict__ bias, int T,
@@ -39,8 +40,8 @@ __global__ __launch_bounds__(64 * kWaves) void router_topk_kernel(const float* _
   __shared__ float cbuf[kWaves][kMaxExperts];  // group-limited routing only
   const int t = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave leaves together
-  router_topk_token(logits, splits, bias, T, E, k, n_group, topk_group, norm, rsf, idx_out, w_out,
-                    ties, t, threadIdx.x & 63, cbuf[threadIdx.x >> 6]);
+  router_topk_token<KPER>(logits, splits, bias, T, E, k, n_group, topk_group, norm, rsf, idx_out,
+                          w_out, ties, t, threadIdx.x & 63, cbuf[threadIdx.x >> 6]);
 }
 
 __global__ void zero_i32_kernel(int32_t* p, int n) {
@@ -54,10 +55,27 @@ hipError_t launch_router_topk(const float* logits, int splits, const float* bias
                               int k, int n_group, int topk_group, int norm, float rsf, int32_t* idx,
                               float* w, int32_t* ties, hipStream_t st) {
   if (T <= 0) return hipSuccess;
+  if (E < 1 || E > kMaxExperts) return hipErrorInvalidValue;
   const int grid = (T + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL(router_topk_kernel, dim3(grid), dim3(64 * kWaves), 0, st, logits,
-                     splits < 1 ? 1 : splits, bias, T, E, k, n_group > 1 ? n_group : 1,
-                     topk_group, norm, rsf, idx, w, ties);
+  const int sp = splits < 1 ? 1 : splits, ng = n_group > 1 ? n_group : 1;
+  switch (router_keys_per_lane(E)) {
+    case 1:
+      hipLaunchKernelGGL(router_topk_kernel<1>, dim3(grid), dim3(64 * kWaves), 0, st, logits, sp,
+                         bias, T, E, k, ng, topk_group, norm, rsf, idx, w, ties);
+      break;
+    case 2:
+      hipLaunchKernelGGL(router_topk_kernel<2>, dim3(grid), dim3(64 * kWaves), 0, st, logits, sp,
+                         bias, T, E, k, ng, topk_group, norm, rsf, idx, w, ties);
+      break;
+    case 4:
+      hipLaunchKernelGGL(router_topk_kernel<4>, dim3(grid), dim3(64 * kWaves), 0, st, logits, sp,
+                         bias, T, E, k, ng, topk_group, norm, rsf, idx, w, ties);
+      break;
+    default:
+      hipLaunchKernelGGL(router_topk_kernel<8>, dim3(grid), dim3(64 * kWaves), 0, st, logits, sp,
+                         bias, T, E, k, ng, topk_group, norm, rsf, idx, w, ties);
+      break;
+  }
   return hipGetLastError();
 }
 

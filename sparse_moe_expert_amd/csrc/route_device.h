@@ -9,12 +9,34 @@
 
 namespace moe {
 
-constexpr int kPer = kMaxExperts / 64;
-
 __device__ __forceinline__ float sigmoidf_acc(float l) { return 1.0f / (1.0f + expf(-l)); }
 
+// Wave-wide maximum of a 32-bit value, returned to every lane (scalar):
+// DPP steps inside each row of 16 lanes (quad xor 1, quad xor 2, half-row
+// mirror, row mirror), then the four row maxima read out and compared.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x141, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x140, 0xF, 0xF, false)));
+  const uint32_t r0 = __builtin_amdgcn_readlane(static_cast<int>(v), 0);
+  const uint32_t r1 = __builtin_amdgcn_readlane(static_cast<int>(v), 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(static_cast<int>(v), 32);
+  const uint32_t r3 = __builtin_amdgcn_readlane(static_cast<int>(v), 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// Keys per lane for E experts (expert e = i * 64 + lane): 1, 2, 4 or 8.
+__host__ __device__ inline int router_keys_per_lane(int E) {
+  return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : 8;
+}
+
 // One wavefront selects the experts of token t.  cw: this wave's LDS row of
-// kMaxExperts floats (group-limited routing stages the keys there).
+// kMaxExperts floats (group-limited routing stages the keys there).  KPER *
+// 64 >= E.  A selection key is the order-preserving 32-bit image of c (0 =
+// no key: taken, outside the allowed groups, or past E); among equal keys
+// the lower expert index wins, as in the oracle's ordering.
+template <int KPER>
 __device__ __forceinline__ void router_topk_token(const float* __restrict__ logits, int splits,
                                                   const float* __restrict__ bias, int T, int E,
                                                   int k, int n_group, int topk_group, int norm,
@@ -24,10 +46,10 @@ __device__ __forceinline__ void router_topk_token(const float* __restrict__ logi
                                                   float* cw) {
   const float* lrow = logits + static_cast<long long>(t) * E;
   const long long split_stride = static_cast<long long>(T) * E;
-  float score[kPer];
-  uint64_t key[kPer];
+  float score[KPER];
+  uint32_t key[KPER];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
+  for (int i = 0; i < KPER; ++i) {
     const int e = i * 64 + lane;
     if (e < E) {
       // split-K partial sums, added in split order (deterministic)
@@ -35,11 +57,11 @@ __device__ __forceinline__ void router_topk_token(const float* __restrict__ logi
       for (int sp = 1; sp < splits; ++sp) l += lrow[sp * split_stride + e];
       score[i] = sigmoidf_acc(l);
       const float c = score[i] + bias[e];
-      key[i] = (static_cast<uint64_t>(f32_order_key(c)) << 32) | static_cast<uint32_t>(~e);
+      key[i] = f32_order_key(c);
       if (n_group > 1) cw[e] = c;
     } else {
       score[i] = 0.f;
-      key[i] = 0;  // below every real key
+      key[i] = 0;
     }
   }
 
@@ -90,7 +112,7 @@ __device__ __forceinline__ void router_topk_token(const float* __restrict__ logi
       }
     }
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = 0; i < KPER; ++i) {
       const int e = i * 64 + lane;
       if (e < E && !((chosen >> (e / G)) & 1ull)) key[i] = 0;
     }
@@ -104,27 +126,38 @@ __device__ __forceinline__ void router_topk_token(const float* __restrict__ logi
 #pragma unroll
   for (int j = 0; j <= kMaxTopK; ++j) {
     if (j >= rounds) continue;
-    uint64_t best = 0;
+    // this lane's best key (its lowest expert among equal keys), then the
+    // wave's best key
+    uint32_t kb = 0;
+    int ib = 0;
+    float sb = 0.f;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const uint64_t o = shfl_xor_u64(best, m);
-      best = o > best ? o : best;
-    }
-    const int e = static_cast<int>(~static_cast<uint32_t>(best));
-    const float c = f32_from_order_key(static_cast<uint32_t>(best >> 32));
-    if (j < k) {
-      // the owner lane retires the key and broadcasts the unbiased score
-      float s_own = 0.f;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        if (lane == (e & 63) && i == (e >> 6)) {
-          s_own = score[i];
-          key[i] = 0;
-        }
+    for (int i = 0; i < KPER; ++i)
+      if (key[i] > kb) {
+        kb = key[i];
+        ib = i;
+        sb = score[i];
       }
-      const float s = __shfl(s_own, e & 63, 64);
+    const uint32_t m = wave_max_u32(kb);
+    // the lowest expert index holding it: lowest slot i, then lowest lane
+    int wl = 0, wi = 0;
+#pragma unroll
+    for (int i = 0; i < KPER; ++i) {
+      const uint64_t hit = __ballot(kb == m && ib == i);
+      if (hit) {
+        wl = static_cast<int>(__builtin_ctzll(hit));
+        wi = i;
+        break;
+      }
+    }
+    const int e = wi * 64 + wl;
+    const float c = f32_from_order_key(m);
+    if (j < k) {
+      // the owner lane retires the key; the unbiased score is read from it
+#pragma unroll
+      for (int i = 0; i < KPER; ++i)
+        if (lane == wl && i == wi) key[i] = 0;
+      const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sb), wl));
       if (j < kMaxTopK) {
         chosen_e[j] = e;
         chosen_s[j] = s;
