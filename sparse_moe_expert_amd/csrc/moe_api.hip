@@ -341,7 +341,7 @@ Layout make_layout(const moe_config_t& c) {
     L.gu = TileShape{128, 256};
     L.dn = TileShape{128, 512};
   }
-  L.router = TileShape{T <= 2048 ? 16 : 64, 64};
+  L.router = TileShape{64, T <= 2048 ? 128 : 64};
   L.router_splits = 1;
   if (c.act_dtype == MOE_BF16 && T >= 4096) {
     L.router = TileShape{128, 512};  // gemm_big.hip: one 512-row weight tile
@@ -358,10 +358,13 @@ Layout make_layout(const moe_config_t& c) {
     }
   } else {
     // Few output tiles (small T): split K so that the launch fills the chip.
-    // The partial sums are added in split order by the top-k kernel.
+    // The partial sums are added in split order by the top-k kernel, which
+    // loads them 8 splits at a time.  Measured at T=256 (route stage, logits
+    // + top-k): 16x64 tiles split 8 ways 38 us, 64x128 tiles split 20 ways
+    // 33 us; 40 ways cost more in the top-k than they save in the GEMM.
     const size_t tiles = ((T + L.router.bm - 1) / L.router.bm) * ((E + L.router.bn - 1) / L.router.bn);
     const int nk = static_cast<int>(H * asz / 128);  // 128-byte K-stages
-    for (int d = 8; d > 1; --d) {
+    for (int d = 20; d > 1; --d) {
       if (nk % d == 0 && nk / d >= 4 && tiles * d <= 1024) {
         L.router_splits = d;
         break;

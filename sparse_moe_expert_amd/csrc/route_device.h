@@ -48,14 +48,31 @@ __device__ __forceinline__ void router_topk_token(const float* __restrict__ logi
   const long long split_stride = static_cast<long long>(T) * E;
   float score[KPER];
   uint32_t key[KPER];
+  // split-K partial sums, added in split order (deterministic); the loads of
+  // up to 8 splits are issued before their adds
+  float l[KPER];
+#pragma unroll
+  for (int i = 0; i < KPER; ++i) l[i] = (i * 64 + lane < E) ? lrow[i * 64 + lane] : 0.f;
+  for (int sp = 1; sp < splits; sp += 8) {
+    float part[KPER][8];
+#pragma unroll
+    for (int i = 0; i < KPER; ++i)
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        part[i][q] = (sp + q < splits && i * 64 + lane < E)
+                         ? lrow[(sp + q) * split_stride + i * 64 + lane]
+                         : 0.f;
+#pragma unroll
+    for (int i = 0; i < KPER; ++i)
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (sp + q < splits) l[i] += part[i][q];
+  }
 #pragma unroll
   for (int i = 0; i < KPER; ++i) {
     const int e = i * 64 + lane;
     if (e < E) {
-      // split-K partial sums, added in split order (deterministic)
-      float l = lrow[e];
-      for (int sp = 1; sp < splits; ++sp) l += lrow[sp * split_stride + e];
-      score[i] = sigmoidf_acc(l);
+      score[i] = sigmoidf_acc(l[i]);
       const float c = score[i] + bias[e];
       key[i] = f32_order_key(c);
       if (n_group > 1) cw[e] = c;
