@@ -140,7 +140,8 @@ def time_layer(lay, steps, warmup, timed_events=True):
     synchronisations (the step time), then K more with HIP events recorded at
     the stage boundaries on the layer's stream (the stage times; the events
     themselves add ~25-50 us to a step, so they stay out of the first pass).
-    Returns (step ms, instrumented step ms, event step ms, stage ms, counts)."""
+    Returns (step ms, instrumented step ms, event step ms, stage ms, counts,
+    p10/p50/p90 of the per-step event times)."""
     import torch
     import sparse_moe_expert_amd as moe
     out = lay.empty_out()
@@ -167,8 +168,14 @@ def time_layer(lay, steps, warmup, timed_events=True):
     names = ["route", "dispatch", "quant_x", "gate_up_gemm", "down_gemm", "combine"]
     stage = {n: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps
              for j, n in enumerate(names)}
-    step_ev = sum(ev[i][0].elapsed_time(ev[i][6]) for i in range(steps)) / steps
-    return plain, wall * 1e3 / steps, step_ev, stage, counts.cpu().numpy()
+    per_step = sorted(ev[i][0].elapsed_time(ev[i][6]) for i in range(steps))
+    step_ev = sum(per_step) / steps
+
+    def pct(q):
+        return per_step[min(steps - 1, int(round(q * (steps - 1))))]
+
+    spread = {"p10": round(pct(0.1), 4), "p50": round(pct(0.5), 4), "p90": round(pct(0.9), 4)}
+    return plain, wall * 1e3 / steps, step_ev, stage, counts.cpu().numpy(), spread
 
 
 def time_calls(fn, iters, warmup):
@@ -301,7 +308,7 @@ def main():
     torch.cuda.synchronize()
 
     log(f"bench: {args.warmup} warmup + {args.steps} timed steps")
-    ms, ms_inst, ms_ev, stage, counts = time_layer(lay, args.steps, args.warmup)
+    ms, ms_inst, ms_ev, stage, counts, spread = time_layer(lay, args.steps, args.warmup)
     flops = cfg.flops()
     dtype = cfg.expert if cfg.expert != "f32" else "f32"
     res = {
@@ -324,6 +331,7 @@ def main():
         "frac_of_peak_mfma_whole_step": round(flops / (ms / 1e3) / 1e12 / PEAK_TFLOPS[dtype], 4),
         "ms_per_step_instrumented": round(ms_inst, 4),
         "ms_per_step_events": round(ms_ev, 4),
+        "ms_per_step_events_p10_p50_p90": spread,
         "stages_ms": {k: round(v, 4) for k, v in stage.items()},
         "rows_per_expert": {"max": int(counts.max()), "mean": float(counts.mean()),
                             "empty": int((counts == 0).sum())},
@@ -339,7 +347,7 @@ def main():
         inp1 = generate(cfg1, weights=False)
         lay1 = _view(lay, cfg1, inp1)
         log(f"bench: decode T={cfg1.T}: {args.decode_steps} steps")
-        ms1, ms1_inst, _, stage1, counts1 = time_layer(lay1, args.decode_steps, 5)
+        ms1, ms1_inst, _, stage1, counts1, spread1 = time_layer(lay1, args.decode_steps, 5)
         b1 = layer_bytes(cfg1, counts1)
         gbs = b1 / (ms1 / 1e3) / 1e9
         # the same layer as one cooperative launch
@@ -352,6 +360,7 @@ def main():
         res["decode_T256"] = {
             "workload": cfg1.name, "ms_per_step": round(ms1, 4),
             "ms_per_step_instrumented": round(ms1_inst, 4),
+            "ms_per_step_events_p10_p50_p90": spread1,
             "fused_single_launch": {"ms_per_step": round(msf, 4), "hbm_GBps": round(gbf, 1),
                                     "frac_of_hbm_peak": round(gbf / PEAK_HBM_GBS, 4)},
             "tokens_per_s": round(cfg1.T / (ms1 / 1e3), 1),
