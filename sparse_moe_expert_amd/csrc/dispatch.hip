@@ -61,16 +61,30 @@ __device__ int block_exclusive_scan(int v, int* sh, int* total) {
   return incl - v;
 }
 
-__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ chunk_counts,
-                                                             int nchunks, int E,
-                                                             int32_t* __restrict__ chunk_base,
-                                                             int32_t* __restrict__ counts,
-                                                             int32_t* __restrict__ offsets) {
+__device__ void build_groups_body(const int32_t* offsets, int T, int k, int E, int S,
+                                  GroupDesc* __restrict__ groups, int32_t* __restrict__ totals,
+                                  int32_t* __restrict__ mtg_gu, int32_t* __restrict__ mtg_dn,
+                                  int bm_gu, int bm_dn, const char* w_gu, const float* s_gu,
+                                  const char* w_dn, const float* s_dn, const char* w_sh_gu,
+                                  const float* s_sh_gu, const char* w_sh_dn, const float* s_sh_dn,
+                                  int H, int I, int esz, int fp8, int* sh);
+
+// Scan over chunks and experts; then (if groups is set) the tile table from
+// the offsets it just formed, in the same block: one launch less than a
+// separate tile-table kernel.
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(
+    const int32_t* __restrict__ chunk_counts, int nchunks, int E, int32_t* __restrict__ chunk_base,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int T, int k, int S,
+    GroupDesc* __restrict__ groups, int32_t* __restrict__ totals, int32_t* __restrict__ mtg_gu,
+    int32_t* __restrict__ mtg_dn, int bm_gu, int bm_dn, const char* w_gu, const float* s_gu,
+    const char* w_dn, const float* s_dn, const char* w_sh_gu, const float* s_sh_gu,
+    const char* w_sh_dn, const float* s_sh_dn, int H, int I, int esz, int fp8) {
   // Thread e walks expert e's column of chunk counts twice (total, then the
   // running bases).  Loads go out 16 chunks at a time so that their latencies
   // overlap instead of adding up chunk by chunk.
   constexpr int B = 16;
   __shared__ int sh[1024];
+  __shared__ int32_t s_off[kMaxExperts + 1];
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
@@ -102,6 +116,13 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
     }
   }
   if (e == 0) offsets[E] = total;
+  if (groups) {
+    if (e < E) s_off[e] = excl;
+    if (e == 0) s_off[E] = total;
+    __syncthreads();
+    build_groups_body(s_off, T, k, E, S, groups, totals, mtg_gu, mtg_dn, bm_gu, bm_dn, w_gu, s_gu,
+                      w_dn, s_dn, w_sh_gu, s_sh_gu, w_sh_dn, s_sh_dn, H, I, esz, fp8, sh);
+  }
 }
 
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __restrict__ idx,
@@ -332,16 +353,16 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int T, int k, int E, int S,
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, chunk_counts, nchunks, E,
-                     chunk_base, counts, offsets);
+                     chunk_base, counts, offsets, T, k, S, groups, totals, mtg_gu, mtg_dn, gu.bm,
+                     dn.bm, static_cast<const char*>(w_gu), s_gu, static_cast<const char*>(w_dn),
+                     s_dn, static_cast<const char*>(w_sh_gu), s_sh_gu,
+                     static_cast<const char*>(w_sh_dn), s_sh_dn, H, I,
+                     static_cast<int>(kind_size(expert_kind)), expert_kind == K_FP8 ? 1 : 0);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(blocks), dim3(256), 0, st, topk_idx, n, E,
                      nchunks, chunk_base, perm, inv);
-  err = hipGetLastError();
-  if (err != hipSuccess || groups == nullptr) return err;
-  return launch_groups_only(offsets, T, k, E, S, groups, totals, mtg_gu, mtg_dn, gu, dn, w_gu,
-                            s_gu, w_dn, s_dn,
-                            w_sh_gu, s_sh_gu, w_sh_dn, s_sh_dn, H, I, expert_kind, st);
+  return hipGetLastError();
 }
 
 }  // namespace moe
