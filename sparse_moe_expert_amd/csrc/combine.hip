@@ -27,7 +27,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       int S) {
   __shared__ float ws[kMaxTopK];
   __shared__ long long rs[kMaxTopK];
-  combine_token<OK>(y, ysh, w, inv, residual, out, T, H, k, S, blockIdx.x, ws, rs);
+  // block (t, part): a 1/gridDim.y share of token t's columns
+  const int per = (H / static_cast<int>(gridDim.y) + 3) & ~3;
+  const int c0 = static_cast<int>(blockIdx.y) * per;
+  const int c1 = min(H, c0 + per);
+  combine_token<OK>(y, ysh, w, inv, residual, out, T, H, k, S, blockIdx.x, ws, rs, c0, c1);
 }
 
 // 16 lanes per 128-channel block, 8 channels per lane.
@@ -73,11 +77,16 @@ hipError_t launch_combine(int act_kind, const void* y, const void* ysh, const fl
   if (T <= 0) return hipSuccess;
   const float* yf = static_cast<const float*>(y);
   const float* yshf = static_cast<const float*>(ysh);
+  // Small batches: split each token's columns over up to 4 blocks (at least
+  // 1024 columns each) so that the launch has ~1024 blocks.  Measured at
+  // T=256: one block per token 14 us.
+  int parts = 1;
+  while (parts < 4 && static_cast<long long>(T) * parts < 1024 && H / (2 * parts) >= 1024) parts *= 2;
   if (act_kind == K_BF16)
-    hipLaunchKernelGGL(combine_kernel<K_BF16>, dim3(T), dim3(256), 0, st, yf, yshf, w, inv,
-                       residual, out, T, H, k, S);
+    hipLaunchKernelGGL(combine_kernel<K_BF16>, dim3(T, parts), dim3(256), 0, st, yf, yshf, w,
+                       inv, residual, out, T, H, k, S);
   else
-    hipLaunchKernelGGL(combine_kernel<K_F32>, dim3(T), dim3(256), 0, st, yf, yshf, w, inv,
+    hipLaunchKernelGGL(combine_kernel<K_F32>, dim3(T, parts), dim3(256), 0, st, yf, yshf, w, inv,
                        residual, out, T, H, k, S);
   return hipGetLastError();
 }

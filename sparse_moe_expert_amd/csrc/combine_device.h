@@ -9,8 +9,11 @@
 
 namespace moe {
 
-// Token t, by one workgroup (every thread of it calls this; it holds one
-// workgroup barrier).  ws / rs: kMaxTopK entries of LDS each.
+// Columns [c0, c1) of token t (multiples of 4), by one workgroup (every
+// thread of it calls this; it holds one workgroup barrier).  ws / rs:
+// kMaxTopK entries of LDS each.  Each output element is summed by one thread
+// in the fixed order (residual, shared experts, slots j ascending), so the
+// column split does not change the result.
 template <int OK>
 __device__ __forceinline__ void combine_token(const float* __restrict__ y,
                                               const float* __restrict__ ysh,
@@ -18,13 +21,13 @@ __device__ __forceinline__ void combine_token(const float* __restrict__ y,
                                               const int32_t* __restrict__ inv,
                                               const void* __restrict__ residual,
                                               void* __restrict__ out, int T, int H, int k, int S,
-                                              int t, float* ws, long long* rs) {
+                                              int t, float* ws, long long* rs, int c0, int c1) {
   if (threadIdx.x < k) {
     ws[threadIdx.x] = w[static_cast<long long>(t) * k + threadIdx.x];
     rs[threadIdx.x] = inv[static_cast<long long>(t) * k + threadIdx.x];
   }
   __syncthreads();
-  for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
+  for (int c = c0 + threadIdx.x * 4; c < c1; c += blockDim.x * 4) {
     float4 acc = float4{0.f, 0.f, 0.f, 0.f};
     if (residual) {
       // decoder block: the residual stream comes first

@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
     __shared__ long long s_r[kMaxTopK];
     for (int t = blockIdx.x; t < a.T; t += gridDim.x) {
       combine_token<K_BF16>(a.y, a.ysh, a.tw, a.inv, a.residual, a.out, a.T, a.H, a.k, a.S, t,
-                            s_w, s_r);
+                            s_w, s_r, 0, a.H);
       __syncthreads();  // s_w / s_r are rewritten for the next token
     }
   }

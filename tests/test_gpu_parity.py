@@ -110,6 +110,26 @@ def test_route_matches_oracle(cid):
     assert t.min() >= 0 and t.max() <= cfg.T
 
 
+@pytest.mark.parametrize("E,k", [(512, 16), (320, 8), (96, 6), (33, 4)])
+def test_route_expert_counts(E, k):
+    """Routing on expert counts that give 8, 5 of 8, 2 and 1 keys per lane
+    (expert e = slot * 64 + lane), including a partly filled last slot."""
+    cfg = small(T=300, H=256, E=E, S=1, k=k, I=128)
+    log(f"route E={E} k={k}: T={cfg.T}")
+    inp = generate(cfg, weights=False)
+    c = ccfg(cfg)
+    x = to_device(inp["x"], cfg.act)
+    w = moe.make_weights(w_router=to_device(inp["w_router"], cfg.act),
+                         router_bias=to_device(inp["bias"], "f32"))
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    moe.moe_route(c, x, w, idx, tw, None, workspace(c))
+    torch.cuda.synchronize()
+    r = oracle.route_inputs(cfg, inp)
+    n = check_routing(cfg, r, idx.cpu().numpy(), tw.cpu().numpy(), f"route E={E}")
+    log(f"route E={E}: near-tie tokens {n}")
+
+
 # ------------------------------------------------------------------ dispatch
 
 def _dispatch_cases():
