@@ -8,19 +8,21 @@
 // forward of the Deep Dive §3.1; routed_scaling_factor from the Transformers
 // Dots1 article's «MoE 路由与专家相关字段» table.
 //
-// Each lane holds E/64 keys.  A round picks the largest (key, -index) pair of
-// the wave with a 6-step xor-shuffle max over a 64-bit packed key (an
-// order-preserving integer image of the fp32 key in the high half, the
-// complemented expert index in the low half, so equal keys go to the lower
-// index).  k rounds pick the experts in slot order; one more round reads the
-// (k+1)-th key for the near-tie count.
+// Each lane holds E/64 keys (expert e = slot * 64 + lane), as the
+// order-preserving 32-bit integer image of the fp32 key.  A round takes each
+// lane's best key, the wave maximum by DPP steps inside each 16-lane row and
+// four readlanes, then ballots slot by slot for the lowest expert index
+// holding it, so equal keys go to the lower index.  k rounds pick the experts
+// in slot order; one more round reads the (k+1)-th key for the near-tie
+// count.
 //
 // Group-limited routing (n_group, topk_group of the same Dots1 field table,
 // which maps them to DeepSeek-V3's router): each group's score is the sum of
 // its two largest keys (the table gives no formula; this is DeepSeek-V3's
 // rule).  Lane g computes group g's score from the wave's keys staged in
-// LDS, the same packed-key max picks topk_group groups, and the keys of the
-// experts outside them drop out before the top-k rounds.
+// LDS, a max over packed (group score, complemented group index) keys picks
+// topk_group groups, and the keys of the experts outside them drop out
+// before the top-k rounds.
 #include "route_device.h"
 
 namespace moe {
