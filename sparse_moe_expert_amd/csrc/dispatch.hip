@@ -44,19 +44,35 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __res
     for (int e = lane; e < E; e += 64) chunk_counts[static_cast<long long>(c) * E + e] = hist[wave][e];
 }
 
-// Single block of 1024 threads.  Block-wide exclusive scan helper.
+// Block-wide exclusive scan of one int per thread (blockDim.x a multiple of
+// 64, at most 4096; every thread calls it).  Each wave scans its 64 values
+// with shuffles, one wave scans the wave totals, and each thread adds its
+// wave's base: three barriers instead of two per doubling step.  Integer
+// sums, so the result does not depend on the order.  sh: blockDim.x / 64
+// ints of LDS, free again when the call returns.
 __device__ int block_exclusive_scan(int v, int* sh, int* total) {
-  const int t = threadIdx.x;
-  sh[t] = v;
-  __syncthreads();
-  for (int off = 1; off < static_cast<int>(blockDim.x); off <<= 1) {
-    const int add = (t >= off) ? sh[t - off] : 0;
-    __syncthreads();
-    sh[t] += add;
-    __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = static_cast<int>(blockDim.x) >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
   }
-  const int incl = sh[t];
-  if (total) *total = sh[blockDim.x - 1];
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < nw ? sh[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(w, off, 64);
+      if (lane >= off) w += y;
+    }
+    if (lane < nw) sh[lane] = w;  // inclusive sums of the wave totals
+  }
+  __syncthreads();
+  const int incl = (wave > 0 ? sh[wave - 1] : 0) + x;
+  if (total) *total = sh[nw - 1];
   __syncthreads();
   return incl - v;
 }
