@@ -455,7 +455,7 @@ hipError_t launch_gemm(int a_kind, int out_kind, TileShape ts, const GemmLaunch&
   if (split && (out_kind != K_F32 || dual)) return hipErrorInvalidValue;
   if (gemm_big_supported(a_kind, out_kind, ts, dual))
     return launch_gemm_big(a_kind, out_kind, dual, g, st);
-  if (!split && gemm_decode_supported(a_kind, out_kind, ts, dual))
+  if (gemm_decode_supported(a_kind, out_kind, ts, dual) && (!split || !dual))
     return launch_gemm_decode(ts, dual, g, st);
   if (a_kind == K_F32 && out_kind == K_F32)
     return dual ? launch_shape<K_F32, K_F32, true>(ts, g, st)

@@ -42,8 +42,12 @@ hipError_t launch_decode(const GemmLaunch& g, hipStream_t st) {
   if (total <= 0) return hipSuccess;
   const long long grid = ((total + 7) / 8) * 8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_decode_kernel<MT, DUAL, NT>), dim3(static_cast<unsigned>(grid)),
-                     dim3(256), 0, st, g);
+  // split K: projection only, whole K-blocks per split
+  const int splits = g.k_splits > 1 ? g.k_splits : 1;
+  if (splits > 1 && (DUAL || (g.K / 128) % splits != 0)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_decode_kernel<MT, DUAL, NT>),
+                     dim3(static_cast<unsigned>(grid), static_cast<unsigned>(splits)), dim3(256), 0,
+                     st, g);
   return hipGetLastError();
 }
 

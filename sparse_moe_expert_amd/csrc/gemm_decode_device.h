@@ -32,7 +32,15 @@ __device__ __forceinline__ void decode_tile(const GemmLaunch& p, int b) {
   const int lgrp = lane >> 4;
   const int K = p.K;
   const int N = p.N;
-  const int nkb = K / 128;
+  // split K (fp32 projection only): block row y takes K-blocks
+  // [y * nkb, (y + 1) * nkb) and writes C + y * c_split_stride
+  int nkb = K / 128, kb0 = 0;
+  long long c_off = 0;
+  if (!DUAL && p.k_splits > 1) {
+    nkb /= p.k_splits;
+    kb0 = static_cast<int>(blockIdx.y) * nkb;
+    c_off = static_cast<long long>(blockIdx.y) * p.c_split_stride;
+  }
   const long long rowb_a = p.lda * 2;
   const long long rowb_b = static_cast<long long>(K) * 2;
 
@@ -62,8 +70,8 @@ __device__ __forceinline__ void decode_tile(const GemmLaunch& p, int b) {
   // a 128-wide K-block of bf16 is one 256-byte tile column of the tiled layout
   const int kb_stride_b = p.w_tiled ? kTileRows * kTileBytes : 256;
   auto load = [&](Regs<MT, NT>& R, int kb) {
-    const int off = kb * 256;
-    const int off_b = kb * kb_stride_b;
+    const int off = (kb0 + kb) * 256;
+    const int off_b = (kb0 + kb) * kb_stride_b;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -124,7 +132,7 @@ __device__ __forceinline__ void decode_tile(const GemmLaunch& p, int b) {
           }
         }
       } else {
-        float* dst = reinterpret_cast<float*>(gemm_out_row<4>(p, row));
+        float* dst = reinterpret_cast<float*>(gemm_out_row<4>(p, row)) + c_off;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const int n = wn0 + t * 16 + lrow;

@@ -342,6 +342,10 @@ Layout make_layout(const moe_config_t& c) {
     L.dn = TileShape{128, 512};
   }
   L.router = TileShape{64, T <= 2048 ? 128 : 64};
+  // bf16 at small T: the weight-streaming kernel (gemm_decode.hip), 16 token
+  // rows x 256 experts per block, K split as below
+  const bool router_stream = c.act_dtype == MOE_BF16 && T <= 2048;
+  if (router_stream) L.router = TileShape{16, 256};
   L.router_splits = 1;
   if (c.act_dtype == MOE_BF16 && T >= 4096) {
     L.router = TileShape{128, 512};  // gemm_big.hip: one 512-row weight tile
@@ -365,7 +369,9 @@ Layout make_layout(const moe_config_t& c) {
     const size_t tiles = ((T + L.router.bm - 1) / L.router.bm) * ((E + L.router.bn - 1) / L.router.bn);
     const int nk = static_cast<int>(H * asz / 128);  // 128-byte K-stages
     for (int d = 20; d > 1; --d) {
-      if (nk % d == 0 && nk / d >= 4 && tiles * d <= 1024) {
+      // the streaming kernel splits whole 128-element K-blocks
+      const bool blocks_ok = !router_stream || (H / 128) % d == 0;
+      if (nk % d == 0 && nk / d >= 4 && tiles * d <= 1024 && blocks_ok) {
         L.router_splits = d;
         break;
       }
