@@ -89,7 +89,9 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(4))) float* const_f32_ptr;
 
-template <int AK, int OK, bool DUAL>
+// PARTN (gate/up only): N is not a multiple of the 256-column tile, so the
+// waves of the last n-tile whose columns lie past N skip their work.
+template <int AK, int OK, bool DUAL, bool PARTN>
 __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
   constexpr int BN = DUAL ? 256 : 512;  // output columns per block
   constexpr int ESZ = (AK == K_FP8) ? 1 : 2;
@@ -251,11 +253,12 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
   // whether this wave's row sub-tiles hold rows of the tile and (projection:
   // the router's 256 experts fill half a 512-column tile) whether its weight
   // rows give columns below N; work outside is never stored.  Wave-uniform.
-  // The gate/up tiles are not tested for columns: N = I is a multiple of
-  // the tile width in the workloads, and the test measured 2% slower there.
-  const bool n_act = DUAL || job.n0 + wn * 64 < N;
+  // Gate/up tiles are tested for columns only when N = I is not a multiple
+  // of the tile width (PARTN); a wave's 64 weight rows give h columns
+  // [n0 + wn*32, +32) (bf16) or its 128 rows [n0 + wn8*64, +64) (fp8).
+  const bool n_act = DUAL ? (!PARTN || job.n0 + wn * 32 < N) : job.n0 + wn * 64 < N;
   const bool m_act[2] = {n_act && wm * 64 < job.rows_here, n_act && wm * 64 + 32 < job.rows_here};
-  const bool n_act8 = DUAL || job.n0 + wn8 * 128 < N;
+  const bool n_act8 = DUAL ? (!PARTN || job.n0 + wn8 * 64 < N) : job.n0 + wn8 * 128 < N;
   const bool t_act[1] = {n_act8 && wm8 * 32 < job.rows_here};
 
 #pragma unroll
@@ -514,8 +517,12 @@ hipError_t launch_big(const GemmLaunch& g, hipStream_t st) {
   const long long grid = ((total + 7) / 8) * 8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const unsigned splits = g.k_splits > 1 ? static_cast<unsigned>(g.k_splits) : 1u;
-  hipLaunchKernelGGL((gemm_big_kernel<AK, OK, DUAL>), dim3(static_cast<unsigned>(grid), splits),
-                     dim3(THREADS), 0, st, g);
+  if (DUAL && g.N % BN != 0)
+    hipLaunchKernelGGL((gemm_big_kernel<AK, OK, DUAL, true>),
+                       dim3(static_cast<unsigned>(grid), splits), dim3(THREADS), 0, st, g);
+  else
+    hipLaunchKernelGGL((gemm_big_kernel<AK, OK, DUAL, false>),
+                       dim3(static_cast<unsigned>(grid), splits), dim3(THREADS), 0, st, g);
   return hipGetLastError();
 }
 
