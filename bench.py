@@ -281,7 +281,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the layer runs on one GPU only (asked for --gpus {args.gpus}); "
               "the layer would shard by experts across GPUs, which is not built here.",
               file=sys.stderr)
         sys.exit(2)

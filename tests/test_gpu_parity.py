@@ -281,7 +281,7 @@ def test_layer_forward_small(case):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cid", [1, 2, 3, 4])
 def test_layer_forward_full_size(cid):
-    """Full BASELINE shapes in the launch configuration the benchmark times.
+    """The full workload shapes, in the launch configuration the benchmark times.
     Routing is checked on all tokens, the output on all tokens (C1) or on a
     seeded sample of 128 tokens (the layer is per-token independent, so a
     token's output does not depend on which others are evaluated)."""
