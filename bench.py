@@ -21,6 +21,8 @@ Extra objects in the line:
                routing (8 groups, 4 chosen) next to the plain router.
   block        the decoder block around the layer (RMSNorm, layer, residual
                add in the combine) and the RMSNorm kernel alone against HBM.
+  device_copy  a 2 GiB device-to-device torch copy (reads + writes over
+               its time), as context for the HBM figures.
   row_major_weights  the same layer with the expert weights row-major
                (the timed line uses them packed into 16-row x 256-byte tiles
                once at load time, moe_pack_expert_weights; --weights rows
@@ -192,6 +194,20 @@ def time_calls(fn, iters, warmup):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / iters
+
+
+def device_copy(gib=2.0, iters=5):
+    """A plain device-to-device copy of `gib` GiB with torch's copy kernel:
+    bytes read + written over its event time.  Context for the HBM figures:
+    a copy mixes reads and writes half and half, so it is no ceiling for the
+    read-dominated layer (which streams faster than it)."""
+    import torch
+    n = int(gib * (1 << 30))
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    ms = time_calls(lambda: b.copy_(a), iters, 2)
+    del a, b
+    return {"bytes_per_copy": 2 * n, "ms": round(ms, 4), "GBps": round(2 * n / (ms / 1e3) / 1e9, 1)}
 
 
 def grouped_routing(lay, cfg, n_group=8, topk_group=4, iters=20):
@@ -390,6 +406,7 @@ def main():
         log("bench: grouped routing and block forward")
         res["grouped_routing"] = grouped_routing(lay, cfg)
         res["block"] = block_forward(lay, cfg, min(args.steps, 10))
+        res["device_copy"] = device_copy()
 
     if args.calib_copy_gib > 0:
         n = int(args.calib_copy_gib * (1 << 30))
