@@ -175,3 +175,71 @@ def test_fp8_layer_close_to_unquantised():
             ref[t] += r.w[t, j] * (oracle.swiglu_hidden(x[t:t + 1], wg, wu) @ wd.T)[0]
     rel = oracle.rms(out - ref) / oracle.rms(ref)
     assert 1e-3 < rel < 0.08
+
+
+def _fp8_expert_fixture():
+    """The hand-derived FP8 expert of tests/golden/fp8_expert_by_hand.json as
+    layer inputs in storage format (E = 1 routed expert, k = 1, and the same
+    weights as the one shared expert)."""
+    g = json.load(open(os.path.join(GOLDEN, "fp8_expert_by_hand.json")))
+    T, H, I = g["dims"]["T"], g["dims"]["H"], g["dims"]["I"]
+    x = np.zeros((T, H), np.uint16)
+    x[0, 0] = x[1, 1] = 0x43E0                        # bf16 448.0
+    gu = np.zeros((2 * I, H), np.uint8)
+    gu[:I, 0] = gu[:I, 1] = 0x28                      # 0.25
+    for i, code, _ in g["w_up_codes_token0_column0"]:
+        gu[I + i, 0] = int(code, 16)
+    for i, code, _ in g["w_up_codes_token1_column1"]:
+        gu[I + i, 1] = int(code, 16)
+    s_gu = np.array([[1.0], [1.0], [2.0 ** -10], [2.0 ** -10]], np.float32)
+    dn = np.zeros((H, I), np.uint8)
+    dn[np.arange(H), np.arange(H)] = 0x38             # 1.0
+    dn[np.arange(H), 128 + np.arange(H)] = 0x30       # 0.5
+    s_dn = np.ones((1, 2), np.float32)
+    cfg = SimpleNamespace(T=T, H=H, E=1, S=1, k=1, I=I, Is=I, act="bf16", expert="fp8",
+                          norm_topk_prob=True, routed_scaling_factor=1.0, n_group=1,
+                          topk_group=1)
+    inp = {"x": x, "w_router": np.zeros((1, H), np.uint16), "bias": np.zeros(1, np.float32),
+           "w_gate_up": gu[None], "w_down": dn[None], "s_gate_up": s_gu[None],
+           "s_down": s_dn[None], "w_sh_gate_up": gu[None], "w_sh_down": dn[None],
+           "s_sh_gate_up": s_gu[None], "s_sh_down": s_dn[None]}
+    exp = np.zeros((T, H))
+    unq = np.zeros((T, H))
+    for t in range(T):
+        for o, v in g["expected_y"][f"token{t}"]:
+            exp[t, o] = v
+        for o, v in g["unquantised_y_for_contrast"][f"token{t}"]:
+            unq[t, o] = v
+    return cfg, inp, exp, unq
+
+
+def test_fp8_expert_golden_by_hand():
+    """expert_forward quantises h per token and per 128 channels before the
+    down projection: the hand-derived codes of the fixture, exactly.  Skipping
+    that step gives the unquantised column; quantising along the token axis
+    (one scale per channel) would reproduce h exactly; a single 256-wide block
+    would give token 0's second block the first block's scale 7."""
+    cfg, inp, exp, unq = _fp8_expert_fixture()
+    _, x_e = oracle.layer_inputs(cfg, inp)
+    a = np.zeros((cfg.T, cfg.H))
+    a[0, 0] = a[1, 1] = 448.0
+    np.testing.assert_array_equal(x_e, a)
+    W = oracle.Weights(cfg, inp)
+    y = oracle.expert_forward(cfg, a, *W.expert(0))
+    np.testing.assert_array_equal(y, exp)
+    assert np.any(y != unq)
+    np.testing.assert_array_equal(oracle.expert_forward(cfg, a, *W.expert(cfg.E)), exp)
+
+
+def test_fp8_sorted_rows_and_layer_golden_by_hand():
+    """sorted_expert_rows' FP8 branch and the whole layer on the same fixture:
+    E = k = 1, so every routing weight is 1 and out = y_shared + y_routed."""
+    cfg, inp, exp, _ = _fp8_expert_fixture()
+    res = oracle.layer_forward(cfg, inp)
+    np.testing.assert_array_equal(res.routing.idx, np.zeros((cfg.T, 1), np.int32))
+    np.testing.assert_array_equal(res.routing.w, np.ones((cfg.T, 1)))
+    np.testing.assert_array_equal(res.out, 2.0 * exp)
+    d = oracle.dispatch(res.routing.idx, cfg.E)
+    _, y_s, _, y_sh = oracle.sorted_expert_rows(cfg, inp, res.routing, d)
+    np.testing.assert_array_equal(y_s[d.inv], exp)
+    np.testing.assert_array_equal(y_sh[0], exp)
