@@ -67,7 +67,7 @@ typedef enum {
  * byte order differs; see moe_pack_expert_weights. */
 typedef enum {
   MOE_LAYOUT_ROWS = 0,  /* row-major, as the shapes below state              */
-  MOE_LAYOUT_TILED = 1  /* 16-row x 256-byte tiles (moe_pack_expert_weights) */
+  MOE_LAYOUT_TILED = 1  /* 16-row x 64-byte tiles (moe_pack_expert_weights)  */
 } moe_layout_t;
 
 /* Layer shape and options; field names follow the model config fields
@@ -78,7 +78,10 @@ typedef struct moe_config {
   int32_t E;        /* n_routed_experts; 1..512                             */
   int32_t S;        /* n_shared_experts; 0..4                               */
   int32_t k;        /* num_experts_per_tok; 1..min(E, 16)                   */
-  int32_t I;        /* moe_intermediate_size of a routed expert; mult. of 128 */
+  int32_t I;        /* moe_intermediate_size of a routed expert; mult. of 128;
+                       FP8 experts: at least 512, else MOE_ERR_UNSUPPORTED
+                       (with fewer channels one e4m3 code of h that rounds
+                       the other way at a boundary moves y too much)       */
   int32_t I_shared; /* intermediate size of a shared expert; must equal I   */
   int32_t norm_topk_prob;      /* 1: renormalise the k chosen scores        */
   float routed_scaling_factor; /* multiplies the routing weights            */
@@ -92,8 +95,8 @@ typedef struct moe_config {
                            E / n_group                                       */
   int32_t expert_layout; /* moe_layout_t of the expert weights; TILED needs
                            H and I times the expert element size to be
-                           multiples of 256 bytes (FP8: H, I multiples of
-                           256), else MOE_ERR_UNSUPPORTED                    */
+                           multiples of 64 bytes (always so with H and I
+                           multiples of 128), else MOE_ERR_UNSUPPORTED       */
 } moe_config_t;
 
 /* Weights of one layer (device pointers).
@@ -126,21 +129,22 @@ typedef struct moe_weights {
 /* Expert weight storage [D1 «并行策略字段»: gate_up_proj and down_proj as
  * stacked per-expert matrices].  No arithmetic: copies `count` row-major
  * [rows, cols] matrices of `dtype` elements from src into dst in the
- * MOE_LAYOUT_TILED order.  Each matrix is cut into 16-row x 256-byte tiles
- * (4 KB); tiles are stored row group by row group, and along the row inside
- * a row group; inside a tile each of its 16 rows keeps its 256 bytes
+ * MOE_LAYOUT_TILED order.  Each matrix is cut into 16-row x 64-byte tiles
+ * (1 KB); tiles are stored row group by row group, and along the row inside
+ * a row group; inside a tile each of its 16 rows keeps its 64 bytes
  * contiguous.  So byte b of row r of matrix m lands at
- *   m*rows*rb + (r/16)*16*rb + (b/256)*4096 + (r%16)*256 + b%256,
+ *   m*rows*rb + (r/16)*16*rb + (b/64)*1024 + (r%16)*64 + b%64,
  * rb = cols * element size.  Matrix m starts at the same byte offset in
  * both layouts, so per-expert pointers and the FP8 block scales are
  * unchanged.  Use: pack w_gate_up with (E, 2I, H), w_down with (E, H, I),
  * and the shared ones with S, then set expert_layout = MOE_LAYOUT_TILED.
- * The GEMMs then read each 16-row weight tile as contiguous 4 KB runs.
+ * Every GEMM load instruction (64 lanes x 16 bytes) then reads one whole
+ * tile, 1 KB contiguous, instead of 16 pieces one weight row apart.
  * src and dst: device, 16-byte aligned, not overlapping, count*rows*rb
  * bytes each.  count >= 0 (0: no-op), rows > 0, cols > 0 and dtype a
  * moe_dtype_t, else MOE_ERR_INVALID_ARG (also for null, misaligned or
  * overlapping buffers); rows not a multiple of 16 or rb not a multiple of
- * 256: MOE_ERR_UNSUPPORTED.  Enqueued on `stream`; dst is complete when the
+ * 64: MOE_ERR_UNSUPPORTED.  Enqueued on `stream`; dst is complete when the
  * stream reaches that point. */
 moe_status_t moe_pack_expert_weights(const void* src, void* dst, int64_t count, int32_t rows,
                                      int32_t cols, int32_t dtype, moe_stream_t stream);
@@ -160,6 +164,37 @@ const char* moe_version(void);
  * config is invalid).  moe_route, moe_dispatch, moe_grouped_ffn and
  * moe_combine accept the same workspace; each needs at most this much. */
 size_t moe_workspace_size(const moe_config_t* cfg);
+
+/* The intermediates a layer forward leaves in its workspace, for callers that
+ * inspect or reuse them (each step of [DD §3.1] / [DD §8.2 figure]):
+ *  MOE_WS_TOPK_IDX   int32 [T, k]      router choice (moe_route semantics)
+ *  MOE_WS_TOPK_W     fp32  [T, k]      routing weights
+ *  MOE_WS_COUNTS     int32 [E]         rows per expert (when opt_counts is NULL)
+ *  MOE_WS_OFFSETS    int32 [E + 1]     exclusive scan of the counts
+ *  MOE_WS_PERM       int32 [T*k]       sorted row -> flat (token, slot) index
+ *  MOE_WS_INV        int32 [T*k]       flat index -> sorted row
+ *  MOE_WS_H          [T*k + S*T, I]    h = SiLU(W_g x) * (W_u x) per sorted row
+ *                                      (routed rows first, then shared expert s
+ *                                      token t at row T*k + s*T + t): bf16, fp32
+ *                                      (MOE_F32 experts) or e4m3 codes (FP8)
+ *  MOE_WS_H_SCALES   fp32  [T*k + S*T, I/128]  FP8 only: h = code * scale
+ *  MOE_WS_H_LO       bf16  [T*k + S*T, I]  bf16 experts on the weight-streaming
+ *                                      and mid-size paths only: h - bf16(h),
+ *                                      rounded to bf16 (h enters the down GEMM
+ *                                      as MOE_WS_H + MOE_WS_H_LO)
+ *  MOE_WS_Y          fp32  [T*k, H]    routed expert outputs, sorted rows
+ *  MOE_WS_Y_SHARED   fp32  [S, T, H]   shared expert outputs
+ * Returns the byte offset of `part` inside the workspace of
+ * moe_layer_forward (and of the entry points that share it) for this config,
+ * or (size_t)-1 if the config is invalid, `part` unknown, or the config holds
+ * no such buffer (e.g. MOE_WS_H_SCALES without FP8).  Contents are valid
+ * after the call that writes them, until the next call on that workspace. */
+typedef enum {
+  MOE_WS_TOPK_IDX = 0, MOE_WS_TOPK_W = 1, MOE_WS_COUNTS = 2, MOE_WS_OFFSETS = 3,
+  MOE_WS_PERM = 4, MOE_WS_INV = 5, MOE_WS_H = 6, MOE_WS_H_SCALES = 7, MOE_WS_H_LO = 8,
+  MOE_WS_Y = 9, MOE_WS_Y_SHARED = 10
+} moe_ws_part_t;
+size_t moe_workspace_offset(const moe_config_t* cfg, int32_t part);
 
 /* Router [DD §3.1 steps 1-2; AA «稀疏激活»]: for every token t
  *   l[t,e] = Σ_h x[t,h] * w_router[e,h]      (fp32 accumulate, never bf16)
@@ -203,9 +238,11 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx, int3
  * and for every shared expert s and token t:
  *   y_shared[s, t] = Wd_s (SiLU(Wg_s x_t) * (Wu_s x_t))   fp32 [S, T, H]
  * fp32 accumulation (SiLU in fp32 with the hardware exponential and
- * reciprocal); h is rounded to the activation type (bf16) between the
- * two GEMMs; y stays fp32 so that the layer output is rounded only once, in
- * moe_combine.  FP8: x and h are quantised per token per 128 channels to e4m3
+ * reciprocal); between the two GEMMs h is stored in bf16 -- as two bf16 terms
+ * (h and its residue, ~16 significant bits) where the down GEMM streams its
+ * weights (fewer than ~96 rows per expert), as one term on the large-tile
+ * prefill path -- see MOE_WS_H_LO; y stays fp32 so that the layer output is
+ * rounded only once, in moe_combine.  FP8: x and h are quantised per token per 128 channels to e4m3
  * with scale amax/448 (fp32, see moe_quantize_fp8) before their GEMM; weights
  * use their block scales.  perm and offsets are moe_dispatch outputs (device).
  * Workspace: h and the tile schedule. */

@@ -18,6 +18,7 @@ from .moe_oracle import (E4M3_MAX, E4M3_TABLE, FP8_BLOCK, Dispatch, LayerResult,
                          dequantize_fp8_weight, dispatch, encode_bf16, encode_e4m3,
                          expert_forward, group_scores, layer_forward, layer_inputs,
                          quantize_fp8_rows, rms, rmsnorm, route, route_inputs, sigmoid,
-                         sorted_expert_rows, swiglu_hidden, widen)
+                         selection_weights, sorted_expert_rows, swiglu_hidden, widen,
+                         with_selection)
 
 __all__ = [n for n in dir() if not n.startswith("_")]

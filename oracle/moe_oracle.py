@@ -215,13 +215,33 @@ def route(x: np.ndarray, w_router: np.ndarray, bias: np.ndarray, k: int,
         gap_ord = np.min(cs[:, :k - 1] - cs[:, 1:k], axis=1)
     else:
         gap_ord = np.full(T, np.inf)
-    chosen = np.take_along_axis(s, idx.astype(np.int64), axis=1)
+    w = selection_weights(s, idx, norm_topk_prob, routed_scaling_factor)
+    return Routing(logits, s, c, idx, w, gap_sel, gap_ord, gap_grp)
+
+
+def selection_weights(s: np.ndarray, idx: np.ndarray, norm_topk_prob: bool = True,
+                      routed_scaling_factor: float = 1.0) -> np.ndarray:
+    """Routing weights of a chosen set: the unbiased sigmoid scores of the k
+    chosen experts, renormalised to sum to 1 (norm_topk_prob [AA «稀疏激活»;
+    DD §3.1 division by the sum of the top-k weights]), times
+    routed_scaling_factor [D1 MoE fields]."""
+    chosen = np.take_along_axis(s, np.asarray(idx, dtype=np.int64), axis=1)
     if norm_topk_prob:
         w = chosen / chosen.sum(axis=1, keepdims=True)
     else:
         w = chosen.copy()
-    w = w * routed_scaling_factor
-    return Routing(logits, s, c, idx, w, gap_sel, gap_ord, gap_grp)
+    return w * routed_scaling_factor
+
+
+def with_selection(r: Routing, idx: np.ndarray, norm_topk_prob: bool = True,
+                   routed_scaling_factor: float = 1.0) -> Routing:
+    """The same router scores with another chosen set `idx` [T, k] (where a
+    near-tie admits more than one correct top-k): weights recomputed by
+    selection_weights; logits, scores, keys and gaps kept."""
+    idx = np.asarray(idx, dtype=np.int32)
+    return Routing(r.logits, r.scores, r.keys, idx,
+                   selection_weights(r.scores, idx, norm_topk_prob, routed_scaling_factor),
+                   r.gap_sel, r.gap_ord, r.gap_grp)
 
 
 # --------------------------------------------------------------------------
@@ -344,15 +364,19 @@ class LayerResult:
     tokens: np.ndarray     # token ids covered
 
 
-def layer_forward(cfg, inp: dict, tokens=None) -> LayerResult:
+def layer_forward(cfg, inp: dict, tokens=None, idx=None) -> LayerResult:
     """out[t] = Σ_s shared_s(x_t) + Σ_j w[t,j] · expert_{idx[t,j]}(x_t)
     [DD §3.1 forward; §3.3 "Weighted sum" then "Shared Expert (always) … add"].
     The layer is per-token independent, so a subset of tokens gives exactly
-    the rows of the full result."""
+    the rows of the full result.  idx (optional, [len(tokens), k]) replaces
+    the router's choice, e.g. by another valid top-k of a near-tied token;
+    its weights are then the renormalised scores of that set."""
     tokens = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
     x_r, x_e = layer_inputs(cfg, inp, tokens)
     r = route(x_r, widen(inp["w_router"], cfg.act), inp["bias"], cfg.k,
               cfg.norm_topk_prob, cfg.routed_scaling_factor, cfg.n_group, cfg.topk_group)
+    if idx is not None:
+        r = with_selection(r, idx, cfg.norm_topk_prob, cfg.routed_scaling_factor)
     n, H, k = tokens.size, cfg.H, cfg.k
     W = Weights(cfg, inp)
     y = np.zeros((n, k, H))
@@ -473,16 +497,17 @@ def block_inputs(cfg, inp: dict, gamma: np.ndarray, tokens=None):
     return h, xn_st
 
 
-def block_forward(cfg, inp: dict, gamma: np.ndarray, tokens=None):
+def block_forward(cfg, inp: dict, gamma: np.ndarray, tokens=None, idx=None):
     """out = h + MoE(RMSNorm(h)) [DD §3.3 figure: "Residual + RMSNorm", MoE
-    FFN, "Residual + Output"].  Returns (out fp64 [n, H], LayerResult)."""
+    FFN, "Residual + Output"].  Returns (out fp64 [n, H], LayerResult).
+    idx: optional choice of experts, as for layer_forward."""
     tokens = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
     h, xn_st = block_inputs(cfg, inp, gamma, tokens)
     # the layer on the normalised rows only (x replaced by the normalised subset)
     full = dict(inp)
     full["x"] = np.zeros_like(inp["x"])
     full["x"][tokens] = xn_st
-    res = layer_forward(cfg, full, tokens)
+    res = layer_forward(cfg, full, tokens, idx=idx)
     return h + res.out, res
 
 

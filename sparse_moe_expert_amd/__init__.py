@@ -19,7 +19,9 @@ _BINDING = (
     "moe_layer_forward_timed", "moe_rmsnorm", "moe_block_forward", "moe_layer_forward_fused",
     "moe_quantize_fp8", "moe_route", "moe_weights_t", "moe_workspace_size", "status_string",
     "version", "last_error_detail", "moe_pack_expert_weights", "MOE_LAYOUT_ROWS",
-    "MOE_LAYOUT_TILED",
+    "MOE_LAYOUT_TILED", "moe_workspace_offset", "MOE_WS_TOPK_IDX", "MOE_WS_TOPK_W",
+    "MOE_WS_COUNTS", "MOE_WS_OFFSETS", "MOE_WS_PERM", "MOE_WS_INV", "MOE_WS_H",
+    "MOE_WS_H_SCALES", "MOE_WS_H_LO", "MOE_WS_Y", "MOE_WS_Y_SHARED",
 )
 
 __all__ = list(_BINDING)

@@ -17,9 +17,14 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
+# moe_ws_part_t
+(MOE_WS_TOPK_IDX, MOE_WS_TOPK_W, MOE_WS_COUNTS, MOE_WS_OFFSETS, MOE_WS_PERM, MOE_WS_INV,
+ MOE_WS_H, MOE_WS_H_SCALES, MOE_WS_H_LO, MOE_WS_Y, MOE_WS_Y_SHARED) = range(11)
+WS_NONE = (1 << 64) - 1
 
 # every entry point of include/moe.h
-EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_version", "moe_workspace_size", "moe_route",
+EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_version", "moe_workspace_size",
+           "moe_workspace_offset", "moe_route",
            "moe_dispatch", "moe_grouped_ffn", "moe_expert_gate_up", "moe_expert_down",
            "moe_combine", "moe_quantize_fp8", "moe_layer_forward", "moe_layer_forward_timed",
            "moe_rmsnorm", "moe_block_forward", "moe_layer_forward_fused",
@@ -67,6 +72,7 @@ def _load():
         "moe_version": (ctypes.c_char_p, []),
         "moe_last_error_detail": (ctypes.c_char_p, []),
         "moe_workspace_size": (SZ, [CP]),
+        "moe_workspace_offset": (SZ, [CP, ctypes.c_int32]),
         "moe_route": (ctypes.c_int, [CP, P, WP, I32P, P, I32P, P, SZ, P]),
         "moe_dispatch": (ctypes.c_int, [CP, I32P, I32P, I32P, I32P, I32P, P, SZ, P]),
         "moe_grouped_ffn": (ctypes.c_int, [CP, P, WP, I32P, I32P, P, P, P, SZ, P]),
@@ -147,6 +153,12 @@ def _check(status: int, where: str):
 
 def moe_workspace_size(cfg: moe_config_t) -> int:
     return int(LIB.moe_workspace_size(ctypes.byref(cfg)))
+
+
+def moe_workspace_offset(cfg: moe_config_t, part: int) -> int | None:
+    """Byte offset of an intermediate in the layer workspace, or None."""
+    off = int(LIB.moe_workspace_offset(ctypes.byref(cfg), int(part)))
+    return None if off == WS_NONE else off
 
 
 def _ws(workspace):

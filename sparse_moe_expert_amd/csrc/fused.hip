@@ -61,7 +61,7 @@ __device__ int wave_exclusive_scan(int* a, int n, int lane) {
   return __shfl(incl, 63, 64);
 }
 
-__global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void fused_decode_kernel(FusedArgs a) {
   cg::grid_group grid = cg::this_grid();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -222,8 +222,14 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   {
     const long long ndn = ((static_cast<long long>(a.dn.grid_mtiles_upper) *
                                 ((a.dn.N + 255) / 256) + 7) / 8) * 8;
-    for (long long vb = blockIdx.x; vb < ndn; vb += gridDim.x)
-      decode_tile<1, false, 4>(a.dn, static_cast<int>(vb));
+    // h as two bf16 terms when the layout keeps its residue (gate/up wrote it)
+    if (a.dn.A_lo) {
+      for (long long vb = blockIdx.x; vb < ndn; vb += gridDim.x)
+        decode_tile<1, false, 4, true>(a.dn, static_cast<int>(vb));
+    } else {
+      for (long long vb = blockIdx.x; vb < ndn; vb += gridDim.x)
+        decode_tile<1, false, 4>(a.dn, static_cast<int>(vb));
+    }
   }
   grid.sync();
 

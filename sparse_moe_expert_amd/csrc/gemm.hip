@@ -88,7 +88,9 @@ __device__ __forceinline__ char* out_row_ptr(const GemmLaunch& p, long long row)
   return static_cast<char*>(p.C2) + (row - p.c_split) * p.ldc * OSZ;
 }
 
-template <int AK, int OK, int BM, int BN, bool DUAL>
+// LO: the A operand is a two-term bf16 split (A + A_lo, the down projection of
+// a split h); the A tile then holds BM rows of A followed by BM rows of A_lo.
+template <int AK, int OK, int BM, int BN, bool DUAL, bool LO>
 struct Cfg {
   using Tr = OpTr<AK>;
   static constexpr int WAVES_M = (BM >= 64) ? 2 : 1;
@@ -96,10 +98,11 @@ struct Cfg {
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 16, TN = WN / 16;
   static constexpr int NB = DUAL ? 2 : 1;
+  static constexpr int NA = LO ? 2 : 1;
   static constexpr int BROWS = BN * NB;
-  static constexpr int A_BYTES = BM * 128, B_BYTES = BROWS * 128;
+  static constexpr int A_BYTES = NA * BM * 128, B_BYTES = BROWS * 128;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int A_CHUNKS = BM * 8, B_CHUNKS = BROWS * 8;
+  static constexpr int A_CHUNKS = NA * BM * 8, B_CHUNKS = BROWS * 8;
   static constexpr int A_LOADS = (A_CHUNKS + 255) / 256, B_LOADS = B_CHUNKS / 256;
   static constexpr int LDC = BN + 4;  // fp32 epilogue tile row stride
   static constexpr int EPI_BYTES = BM * LDC * 4;
@@ -111,9 +114,10 @@ struct Cfg {
   static_assert(128 % BN == 0 || BN % 128 == 0, "BN must tile 128-wide scale blocks");
 };
 
-template <int AK, int OK, int BM, int BN, bool DUAL>
+template <int AK, int OK, int BM, int BN, bool DUAL, bool LO>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
-  using C = Cfg<AK, OK, BM, BN, DUAL>;
+  static_assert(!LO || (AK == K_BF16 && OK == K_F32 && !DUAL), "two-term A: bf16 projection");
+  using C = Cfg<AK, OK, BM, BN, DUAL, LO>;
   using Tr = typename C::Tr;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
 
@@ -194,9 +198,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
     a_on[i] = q < C::A_CHUNKS;
     const int r = a_on[i] ? (q >> 3) : 0;
     const int c = q & 7;
-    const int rr = min(r, rows_here - 1);
+    const bool lo = LO && r >= BM;  // rows [BM, 2BM) of the tile: A_lo
+    const int rr = min(lo ? r - BM : r, rows_here - 1);
     const int src = a_source_row(p, row_begin + m0 + rr);
-    a_src[i] = static_cast<const char*>(p.A) + src * row_bytes_a + c * 16;
+    a_src[i] = static_cast<const char*>(lo ? p.A_lo : p.A) + src * row_bytes_a + c * 16;
     a_lds[i] = swz(r, c);
   }
   const char* b_src[C::B_LOADS];
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
     const int c = q & 7;
     const int sb = r / BN;
     const int n = min(n0 + (r - sb * BN), p.N - 1);
-    b_src[i] = W + w_tile_row_off(p.w_tiled, sb * p.N + n, row_bytes_b) + c * 16;
+    b_src[i] = W + w_tile_row_off(p.w_tiled, sb * p.N + n, row_bytes_b) + w_tile_k_off(p.w_tiled, c * 16);
     b_lds[i] = C::A_BYTES + swz(r, c);
   }
   // FP8: row scales of A (one per row and 128-K block) and the W block scales
@@ -226,7 +231,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
   float ras = 0.f;
   auto gload = [&](int kt) {
     const int koff = kt * 128;
-    // a K-stage is 128 bytes, so it never straddles a 256-byte tile column
+    // K-stages start on a 64-byte tile column, so stage and chunk offsets add
     const long long koff_b = w_tile_k_off(p.w_tiled, koff);
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i)
@@ -294,6 +299,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
 #pragma unroll
     for (int s = 0; s < Tr::KSTEPS; ++s) {
       uint4 af[C::TM][Tr::CPL];
+      uint4 af_lo[C::TM];
       uint4 bf[C::NB][C::TN][Tr::CPL];
 #pragma unroll
       for (int tm = 0; tm < C::TM; ++tm) {
@@ -303,6 +309,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
           const int ch = (Tr::CPL == 1) ? (s * 4 + lgrp) : (2 * lgrp + c);
           af[tm][c] = *reinterpret_cast<const uint4*>(As + swz(r, ch));
         }
+        if constexpr (LO) af_lo[tm] = *reinterpret_cast<const uint4*>(As + swz(BM + r, s * 4 + lgrp));
       }
 #pragma unroll
       for (int sb = 0; sb < C::NB; ++sb)
@@ -327,6 +334,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
               acc[sb][tm][tn] += part * sc;
             } else {
               acc[sb][tm][tn] = mma<AK>(af[tm], bf[sb][tn], acc[sb][tm][tn]);
+              if constexpr (LO) acc[sb][tm][tn] = mma<AK>(&af_lo[tm], bf[sb][tn], acc[sb][tm][tn]);
             }
           }
     }
@@ -390,16 +398,34 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
       const int n = n0 + c8;
       const float* src = Cs + r * C::LDC + c8;
       char* dst = out_row_ptr<OK>(p, row_begin + m0 + r);
+      // two-term h: hi = bf16(v), lo = bf16(v - hi) into C_lo (same row)
+      char* dst_lo = p.C_lo ? static_cast<char*>(p.C_lo) + (row_begin + m0 + r) * p.ldc * 2 : nullptr;
       if (n + 8 <= p.N && (p.ldc & 7) == 0) {
+        uint16_t hi[8], lo[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          hi[i] = f32_to_bf16(src[i]);
+          lo[i] = f32_to_bf16(src[i] - bf16_to_f32(hi[i]));
+        }
         uint4 o;
-        o.x = f32_to_bf16(src[0]) | (static_cast<uint32_t>(f32_to_bf16(src[1])) << 16);
-        o.y = f32_to_bf16(src[2]) | (static_cast<uint32_t>(f32_to_bf16(src[3])) << 16);
-        o.z = f32_to_bf16(src[4]) | (static_cast<uint32_t>(f32_to_bf16(src[5])) << 16);
-        o.w = f32_to_bf16(src[6]) | (static_cast<uint32_t>(f32_to_bf16(src[7])) << 16);
+        o.x = hi[0] | (static_cast<uint32_t>(hi[1]) << 16);
+        o.y = hi[2] | (static_cast<uint32_t>(hi[3]) << 16);
+        o.z = hi[4] | (static_cast<uint32_t>(hi[5]) << 16);
+        o.w = hi[6] | (static_cast<uint32_t>(hi[7]) << 16);
         *reinterpret_cast<uint4*>(dst + static_cast<long long>(n) * 2) = o;
+        if (dst_lo) {
+          o.x = lo[0] | (static_cast<uint32_t>(lo[1]) << 16);
+          o.y = lo[2] | (static_cast<uint32_t>(lo[3]) << 16);
+          o.z = lo[4] | (static_cast<uint32_t>(lo[5]) << 16);
+          o.w = lo[6] | (static_cast<uint32_t>(lo[7]) << 16);
+          *reinterpret_cast<uint4*>(dst_lo + static_cast<long long>(n) * 2) = o;
+        }
       } else {
-        for (int i = 0; i < 8 && n + i < p.N; ++i)
-          reinterpret_cast<uint16_t*>(dst)[n + i] = f32_to_bf16(src[i]);
+        for (int i = 0; i < 8 && n + i < p.N; ++i) {
+          const uint16_t hi = f32_to_bf16(src[i]);
+          reinterpret_cast<uint16_t*>(dst)[n + i] = hi;
+          if (dst_lo) reinterpret_cast<uint16_t*>(dst_lo)[n + i] = f32_to_bf16(src[i] - bf16_to_f32(hi));
+        }
       }
     }
   } else {
@@ -421,6 +447,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
 
 template <int AK, int OK, int BM, int BN, bool DUAL>
 hipError_t launch_t(const GemmLaunch& g, hipStream_t st) {
+  constexpr bool kCanLo = AK == K_BF16 && OK == K_F32 && !DUAL;
   const int ntn = (g.N + BN - 1) / BN;
   const long long ub_m =
       g.single_group_rows > 0 ? (g.single_group_rows + BM - 1) / BM : g.grid_mtiles_upper;
@@ -429,8 +456,13 @@ hipError_t launch_t(const GemmLaunch& g, hipStream_t st) {
   const long long grid = ((total + 7) / 8) * 8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const unsigned splits = g.k_splits > 1 ? static_cast<unsigned>(g.k_splits) : 1u;
-  hipLaunchKernelGGL((grouped_gemm_kernel<AK, OK, BM, BN, DUAL>),
-                     dim3(static_cast<unsigned>(grid), splits), dim3(256), 0, st, g);
+  const dim3 gd(static_cast<unsigned>(grid), splits);
+  if (g.A_lo) {
+    if (!kCanLo) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((grouped_gemm_kernel<AK, OK, BM, BN, DUAL, kCanLo>), gd, dim3(256), 0, st, g);
+  } else {
+    hipLaunchKernelGGL((grouped_gemm_kernel<AK, OK, BM, BN, DUAL, false>), gd, dim3(256), 0, st, g);
+  }
   return hipGetLastError();
 }
 
@@ -453,8 +485,14 @@ hipError_t launch_gemm(int a_kind, int out_kind, TileShape ts, const GemmLaunch&
   const bool dual = g.dual != 0;
   const bool split = g.k_splits > 1;  // the generic and large-tile kernels split K
   if (split && (out_kind != K_F32 || dual)) return hipErrorInvalidValue;
-  if (gemm_big_supported(a_kind, out_kind, ts, dual))
+  if (gemm_prefill_supported(a_kind, out_kind, ts, dual)) {
+    if (g.A_lo || g.C_lo) return hipErrorInvalidValue;  // one-term h only
+    return launch_gemm_prefill(dual, g, st);
+  }
+  if (gemm_big_supported(a_kind, out_kind, ts, dual)) {
+    if (g.A_lo || g.C_lo) return hipErrorInvalidValue;  // one-term h only
     return launch_gemm_big(a_kind, out_kind, dual, g, st);
+  }
   if (gemm_decode_supported(a_kind, out_kind, ts, dual) && (!split || !dual))
     return launch_gemm_decode(ts, dual, g, st);
   if (a_kind == K_F32 && out_kind == K_F32)

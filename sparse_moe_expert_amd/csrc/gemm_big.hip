@@ -154,7 +154,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
     } else {
       wr = min(job.n0 + r, N - 1);
     }
-    b_off[i] = static_cast<uint32_t>(w_tile_row_off(p.w_tiled, wr, rowb_b) + lchunk * 16);
+    b_off[i] = static_cast<uint32_t>(w_tile_row_off(p.w_tiled, wr, rowb_b) +
+                                     w_tile_k_off(p.w_tiled, lchunk * 16));
   }
 
   // wave (wm, wn): rows [wm*64, +64) x B-tile rows [wn*64, +64)
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_big_kernel(GemmLaunch p) {
   auto issue = [&](int kt) {
     char* base = smem + (kt % NS) * STAGE;
     const int koff = (kt0 + kt) * 128;
-    // a K-slice is 128 bytes, so it never straddles a 256-byte tile column
+    // K-slices start on a 64-byte tile column, so slice and chunk offsets add
     const int koff_b = static_cast<int>(w_tile_k_off(p.w_tiled, koff));
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i)

@@ -21,14 +21,18 @@
 //  * The expert's token rows (A) come from L2: all waves of the expert read
 //    the same few rows.
 //  * v_mfma_f32_16x16x32_bf16: rows = tokens (lane%16), columns = weight rows.
+//  * h as two bf16 terms: the gate/up epilogue stores hi = bf16(h) and
+//    lo = bf16(h - hi); the projection multiplies both by the same weight
+//    registers (twice the MFMAs and the L2-resident token loads, no extra
+//    weight bytes), so h enters the down GEMM with ~16 significant bits.
 #include "gemm_decode_device.h"
 
 namespace moe {
 namespace {
 
-template <int MT, bool DUAL, int NT>
+template <int MT, bool DUAL, int NT, bool LO>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmLaunch p) {
-  decode_tile<MT, DUAL, NT>(p, blockIdx.x);
+  decode_tile<MT, DUAL, NT, LO>(p, blockIdx.x);
 }
 
 template <int MT, bool DUAL, int NT>
@@ -45,9 +49,11 @@ hipError_t launch_decode(const GemmLaunch& g, hipStream_t st) {
   // split K: projection only, whole K-blocks per split
   const int splits = g.k_splits > 1 ? g.k_splits : 1;
   if (splits > 1 && (DUAL || (g.K / 128) % splits != 0)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_decode_kernel<MT, DUAL, NT>),
-                     dim3(static_cast<unsigned>(grid), static_cast<unsigned>(splits)), dim3(256), 0,
-                     st, g);
+  const dim3 gd(static_cast<unsigned>(grid), static_cast<unsigned>(splits));
+  if (!DUAL && g.A_lo)
+    hipLaunchKernelGGL((gemm_decode_kernel<MT, DUAL, NT, !DUAL>), gd, dim3(256), 0, st, g);
+  else
+    hipLaunchKernelGGL((gemm_decode_kernel<MT, DUAL, NT, false>), gd, dim3(256), 0, st, g);
   return hipGetLastError();
 }
 

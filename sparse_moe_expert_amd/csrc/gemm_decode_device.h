@@ -9,15 +9,19 @@ namespace moe {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-template <int MT, int NT>
+template <int MT, int NT, int NA>
 struct Regs {
-  uint4 a[MT][4];
+  uint4 a[NA][MT][4];  // NA = 2: A and its bf16 residue A_lo
   uint4 b[NT][4];
 };
 
 // One 4-wave tile (block index b, see find_tile_at) of the decode GEMM.
-template <int MT, bool DUAL, int NT>
+// LO (projection only): A is a two-term bf16 split, A + A_lo (p.A_lo), and
+// both terms multiply the same weight fragments.
+template <int MT, bool DUAL, int NT, bool LO = false>
 __device__ __forceinline__ void decode_tile(const GemmLaunch& p, int b) {
+  static_assert(!(DUAL && LO), "the two-term A is the down projection's input");
+  constexpr int NA = LO ? 2 : 1;
   // NT 16-row weight tiles per wave: gate/up holds NT/2 gate tiles and the
   // NT/2 matching up tiles
   constexpr int BM = 16 * MT;
@@ -59,27 +63,33 @@ __device__ __forceinline__ void decode_tile(const GemmLaunch& p, int b) {
     }
     bptr[t] = job.W + w_tile_row_off(p.w_tiled, wr, rowb_b) + lgrp * 16;
   }
-  const char* aptr[MT];
+  const char* aptr[NA][MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int r = min(m * 16 + lrow, job.rows_here - 1);
     const int src = gemm_a_source_row(p, job.row_begin + job.m0 + r);
-    aptr[m] = static_cast<const char*>(p.A) + src * rowb_a + lgrp * 16;
+    aptr[0][m] = static_cast<const char*>(p.A) + src * rowb_a + lgrp * 16;
+    if constexpr (LO) aptr[NA - 1][m] = static_cast<const char*>(p.A_lo) + src * rowb_a + lgrp * 16;
   }
 
-  // a 128-wide K-block of bf16 is one 256-byte tile column of the tiled layout
-  const int kb_stride_b = p.w_tiled ? kTileRows * kTileBytes : 256;
-  auto load = [&](Regs<MT, NT>& R, int kb) {
+  // a 128-wide K-block of bf16 is 256 bytes: four 64-byte tile columns of the
+  // tiled layout, load s reading column s (16 rows x 64 bytes, 1 KB contiguous)
+  const int s_stride_b = static_cast<int>(w_tile_k_off(p.w_tiled, 64));
+  auto load = [&](Regs<MT, NT, NA>& R, int kb) {
     const int off = (kb0 + kb) * 256;
-    const int off_b = (kb0 + kb) * kb_stride_b;
+    const int off_b = static_cast<int>(w_tile_k_off(p.w_tiled, (kb0 + kb) * 256));
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) R.b[t][s] = *reinterpret_cast<const uint4*>(bptr[t] + off_b + s * 64);
+      for (int s = 0; s < 4; ++s)
+        R.b[t][s] = *reinterpret_cast<const uint4*>(bptr[t] + off_b + s * s_stride_b);
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int q = 0; q < NA; ++q)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) R.a[m][s] = *reinterpret_cast<const uint4*>(aptr[m] + off + s * 64);
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          R.a[q][m][s] = *reinterpret_cast<const uint4*>(aptr[q][m] + off + s * 64);
   };
 
   f32x4_t acc[MT][NT];
@@ -88,19 +98,21 @@ __device__ __forceinline__ void decode_tile(const GemmLaunch& p, int b) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[m][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Regs<MT, NT>& R) {
+  auto compute = [&](const Regs<MT, NT, NA>& R) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+      for (int q = 0; q < NA; ++q)
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, R.a[m][s]), __builtin_bit_cast(bf16x8, R.b[t][s]),
-              acc[m][t], 0, 0, 0);
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, R.a[q][m][s]), __builtin_bit_cast(bf16x8, R.b[t][s]),
+                acc[m][t], 0, 0, 0);
   };
 
-  Regs<MT, NT> r0, r1;
+  Regs<MT, NT, NA> r0, r1;
   load(r0, 0);
   int kb = 0;
   for (; kb + 2 <= nkb; kb += 2) {
@@ -127,8 +139,12 @@ __device__ __forceinline__ void decode_tile(const GemmLaunch& p, int b) {
           if (n < N) {
             const float g = acc[m][j][i];
             const float u = acc[m][j + NT / 2][i];
-            reinterpret_cast<uint16_t*>(gemm_out_row<2>(p, row))[n] =
-                f32_to_bf16(silu_mul(g, u));
+            const float h = silu_mul(g, u);
+            const uint16_t hi = f32_to_bf16(h);
+            reinterpret_cast<uint16_t*>(gemm_out_row<2>(p, row))[n] = hi;
+            if (p.C_lo)
+              reinterpret_cast<uint16_t*>(static_cast<char*>(p.C_lo) + row * p.ldc * 2)[n] =
+                  f32_to_bf16(h - bf16_to_f32(hi));
           }
         }
       } else {

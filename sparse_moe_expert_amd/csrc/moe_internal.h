@@ -20,6 +20,7 @@ constexpr int kMaxTopK = 16;
 constexpr int kQBlock = 128;          // FP8 scale granularity along K
 constexpr int kDispatchChunk = 1024;  // flat (token, slot) pairs per dispatch wave
 constexpr float kTieEps = 1e-6f;
+constexpr int kFp8MinI = 512;         // smallest intermediate size run in FP8
 
 // One GEMM group = one expert (routed e < E, shared E + s) over a contiguous
 // range of rows of the sorted row space.  Rows [0, R) are the routed (token,
@@ -60,6 +61,7 @@ struct Layout {
   size_t xq;            // FP8: [T, H] e4m3 codes
   size_t xs;            // FP8: [T, H/128] fp32 scales
   size_t h;             // [R + S*T, I] act type, or e4m3 codes (FP8)
+  size_t hlo;           // bf16 h_split: [R + S*T, I] bf16 residue h - bf16(h)
   size_t hs;            // FP8: [R + S*T, I/128] fp32 scales
   size_t y;             // [R, H] fp32  (routed expert outputs, sorted)
   size_t ysh;           // [S, T, H] fp32
@@ -67,6 +69,7 @@ struct Layout {
   size_t total;
   int nchunks;
   int router_splits;    // >= 1
+  bool h_split;         // bf16 h kept as hi + lo (down GEMM on an HBM-bound kernel)
   TileShape gu, dn, router;
 };
 
@@ -75,19 +78,22 @@ Layout make_layout(const moe_config_t& c);
 inline size_t kind_size(int kind) { return kind == K_F32 ? 4 : kind == K_BF16 ? 2 : 1; }
 
 // Tiled weight storage: a row-major [rows, K] matrix (rows a multiple of 16,
-// K * element size a multiple of 256 bytes) cut into 16-row x 256-byte tiles
-// of 4 KB.  Tiles are stored row group by row group, and along K inside a
-// row group; inside a tile each row's 256 bytes are contiguous.  The byte
-// offset of (row, byte b of the row) splits into a row part and a K part,
-// which the kernels add separately; b % 256 carries into no other field.
+// K * element size a multiple of 64 bytes) cut into 16-row x 64-byte tiles
+// of 1 KB.  Tiles are stored row group by row group, and along K inside a
+// row group; inside a tile each row's 64 bytes are contiguous.  One GEMM
+// load instruction of 64 lanes x 16 bytes then reads one tile, 1 KB
+// contiguous.  The byte offset of (row, byte b of the row) splits into a row
+// part and a K part, which the kernels add separately; for K offsets that
+// are multiples of 64 the K part is additive (w_tile_k_off(a + b) =
+// w_tile_k_off(a) + w_tile_k_off(b) when a % 64 == 0).
 constexpr int kTileRows = 16;
-constexpr int kTileBytes = 256;
+constexpr int kTileBytes = 64;
 __host__ __device__ inline long long w_tile_row_off(int tiled, int row, long long row_bytes) {
   return tiled ? static_cast<long long>(row >> 4) * (row_bytes * kTileRows) + (row & 15) * kTileBytes
                : static_cast<long long>(row) * row_bytes;
 }
 __host__ __device__ inline long long w_tile_k_off(int tiled, long long kbyte) {
-  return tiled ? (kbyte >> 8) * (kTileRows * kTileBytes) + (kbyte & 255) : kbyte;
+  return tiled ? (kbyte >> 6) * (kTileRows * kTileBytes) + (kbyte & 63) : kbyte;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -120,19 +126,28 @@ struct GemmLaunch {
   long long c_split;
   long long ldc;
   float* c_scale;          // FP8 output scales [rows, N/128]
+  // two-term bf16 h (gate/up writes, down reads; null = one term): the gate/up
+  // output v is stored as hi = bf16(v) in C and lo = bf16(v - hi) in C_lo (same
+  // row indexing, no C2 split); the down GEMM adds W * A_lo to W * A, A_lo
+  // with the stride and row mapping of A
+  void* C_lo;
+  const void* A_lo;
   // split K (generic kernel, fp32 output only): block y computes the K range
   // [y * K / k_splits, (y + 1) * K / k_splits) into C + y * c_split_stride
   int k_splits;            // 0 or 1: no split
   long long c_split_stride;  // elements
-  // expert weights (groups' w_gu / w_dn) stored as 16-row x 256-byte tiles
+  // expert weights (groups' w_gu / w_dn) stored as 16-row x 64-byte tiles
   // (w_tile_row_off / w_tile_k_off); the router's b_single is always row-major
   int w_tiled;
 };
 
 hipError_t launch_gemm(int a_kind, int out_kind, TileShape ts, const GemmLaunch& g,
                        hipStream_t st);
-// Large-tile bf16 / fp8 kernel (gemm_big.hip): 128 rows x 256 h-columns
-// (gate/up) or 128 rows x 512 output columns (projection).
+// Large-tile bf16 kernel (gemm_prefill.hip): 128 rows x 256 h-columns
+// (gate/up) or 128 rows x 512 output columns (projection), bf16 operands.
+bool gemm_prefill_supported(int a_kind, int out_kind, TileShape ts, bool dual);
+hipError_t launch_gemm_prefill(bool dual, const GemmLaunch& g, hipStream_t st);
+// Large-tile fp8 kernel (gemm_big.hip), same tile shapes.
 bool gemm_big_supported(int a_kind, int out_kind, TileShape ts, bool dual);
 hipError_t launch_gemm_big(int a_kind, int out_kind, bool dual, const GemmLaunch& g,
                            hipStream_t st);

@@ -1,12 +1,14 @@
 // Expert weights rearranged into the tiled storage of moe_internal.h
-// (w_tile_row_off / w_tile_k_off): 16-row x 256-byte tiles, 4 KB each.
+// (w_tile_row_off / w_tile_k_off): 16-row x 64-byte tiles, 1 KB each.
 //
 // A pure byte permutation, done once when the weights are loaded.  With it
-// each 16-row weight tile that a GEMM wave streams is one contiguous 4 KB
-// run per 256 bytes of K, instead of 16 row pieces 2*K bytes apart.
+// the 16 rows x 64 bytes that one GEMM load instruction (64 lanes x 16
+// bytes) reads are one contiguous 1 KB run instead of 16 row pieces 2*K
+// bytes apart: the address unit handles one contiguous kilobyte much faster
+// than sixteen scattered pieces.
 //
 // One thread moves one 16-byte chunk.  Threads walk the output in order, so
-// the stores are contiguous; 16 neighbouring threads read one row's 256
+// the stores are contiguous; 4 neighbouring threads read one row's 64
 // contiguous bytes.  Grid-stride loop over all chunks of all matrices.
 #include "moe_internal.h"
 

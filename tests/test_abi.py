@@ -84,17 +84,20 @@ def cfg(**kw):
 @pytest.mark.parametrize("kw,ok", [
     (dict(), True),
     (dict(act="bf16", expert="bf16"), True),
-    (dict(act="bf16", expert="fp8"), True),
+    (dict(act="bf16", expert="fp8", I=512), True),
+    # FP8 needs I >= 512 (re-quantised h: one boundary code is too large a share of y below)
+    (dict(act="bf16", expert="fp8"), False), (dict(act="bf16", expert="fp8", I=384), False),
     (dict(T=0), True),
     (dict(E=0), False), (dict(k=0), False), (dict(k=33), False), (dict(E=513, k=4), False),
     (dict(k=17, E=64), False), (dict(H=500), False), (dict(I=100), False), (dict(S=5), False),
     (dict(I_shared=256), False), (dict(act="f32", expert="bf16"), False),
     (dict(act="bf16", expert="f32"), False), (dict(T=-1), False),
-    # tiled expert weights need whole 256-byte tile columns along H and I
+    # tiled expert weights need whole 64-byte tile columns along H and I (always
+    # so with multiples of 128 elements)
     (dict(tiled=True), True), (dict(act="bf16", expert="bf16", tiled=True), True),
-    (dict(act="bf16", expert="fp8", tiled=True), False),         # I = 128 fp8 = 128 bytes
-    (dict(act="bf16", expert="fp8", I=256, tiled=True), True),
-    (dict(act="bf16", expert="fp8", H=640, I=256, tiled=True), False),
+    (dict(act="bf16", expert="fp8", I=640, tiled=True), True),
+    (dict(act="bf16", expert="fp8", I=512, tiled=True), True),
+    (dict(act="bf16", expert="fp8", H=640, I=512, tiled=True), True),
 ])
 def test_workspace_size_validates(kw, ok):
     n = moe.moe_workspace_size(cfg(**kw))
@@ -148,9 +151,14 @@ def test_validation_rejects_before_launch():
     bad = cfg(H=640 + 64)
     assert call("moe_layer_forward", by(bad), by(w), FAKE, FAKE, None, None, FAKE, n, None) == moe.MOE_ERR_UNSUPPORTED
     # fp8 needs its block scales
-    c8 = cfg(act="bf16", expert="fp8")
+    c8 = cfg(act="bf16", expert="fp8", I=512)
     n8 = moe.moe_workspace_size(c8)
     assert call("moe_layer_forward", by(c8), by(w), FAKE, FAKE, None, None, FAKE, n8, None) == moe.MOE_ERR_INVALID_ARG
+    # fp8 below I = 512 is refused before anything is checked or enqueued
+    c8s = cfg(act="bf16", expert="fp8", I=256)
+    w8 = weights(s_gate_up=FAKE, s_down=FAKE, s_sh_gate_up=FAKE, s_sh_down=FAKE)
+    for name in ("moe_layer_forward", "moe_layer_forward_fused"):
+        assert call(name, by(c8s), by(w8), FAKE, FAKE, None, None, FAKE, n8, None) == moe.MOE_ERR_UNSUPPORTED
     # combine / dispatch / quantiser argument checks
     assert call("moe_combine", by(c), FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert call("moe_dispatch", by(c), FAKE, None, FAKE, FAKE, FAKE, FAKE, n, None) == moe.MOE_ERR_INVALID_ARG
@@ -224,8 +232,9 @@ def test_pack_validation():
     assert call(P, A, B, 1, 16, 0, moe.MOE_BF16, None) == moe.MOE_ERR_INVALID_ARG
     assert call(P, A, B, 1, 16, 128, 7, None) == moe.MOE_ERR_INVALID_ARG
     assert call(P, A, B, 1, 24, 128, moe.MOE_BF16, None) == moe.MOE_ERR_UNSUPPORTED  # rows % 16
-    assert call(P, A, B, 1, 16, 64, moe.MOE_BF16, None) == moe.MOE_ERR_UNSUPPORTED   # 128-byte rows
-    assert call(P, A, B, 1, 16, 128, moe.MOE_FP8_E4M3, None) == moe.MOE_ERR_UNSUPPORTED
+    assert call(P, A, B, 1, 16, 40, moe.MOE_BF16, None) == moe.MOE_ERR_UNSUPPORTED   # 80-byte rows
+    assert call(P, A, B, 1, 16, 96, moe.MOE_FP8_E4M3, None) == moe.MOE_ERR_UNSUPPORTED
+    assert call(P, A, B, 0, 16, 32, moe.MOE_BF16, None) == moe.MOE_OK               # 64-byte rows
     assert call(P, None, B, 1, 16, 128, moe.MOE_BF16, None) == moe.MOE_ERR_INVALID_ARG
     assert call(P, A, None, 1, 16, 128, moe.MOE_BF16, None) == moe.MOE_ERR_INVALID_ARG
     assert call(P, A + 8, B, 1, 16, 128, moe.MOE_BF16, None) == moe.MOE_ERR_INVALID_ARG
@@ -233,3 +242,31 @@ def test_pack_validation():
     assert call(P, A, A + 2048, 1, 16, 128, moe.MOE_BF16, None) == moe.MOE_ERR_INVALID_ARG
     # byte count overflowing int64
     assert call(P, A, B, 1 << 62, 16, 128, moe.MOE_BF16, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_offsets():
+    """moe_workspace_offset: every part lies inside the workspace, in the order
+    of the carve-out; h's bf16 residue exists only where the down GEMM streams
+    its weights (not on the T=16384 large-tile path, not for fp8 or fp32)."""
+    parts = [moe.MOE_WS_TOPK_IDX, moe.MOE_WS_TOPK_W, moe.MOE_WS_COUNTS, moe.MOE_WS_OFFSETS,
+             moe.MOE_WS_PERM, moe.MOE_WS_INV, moe.MOE_WS_H, moe.MOE_WS_H_LO, moe.MOE_WS_Y,
+             moe.MOE_WS_Y_SHARED]
+    dec = moe.make_config(T=256, H=5120, E=256, S=1, k=8, I=1536)
+    n = moe.moe_workspace_size(dec)
+    offs = [moe.moe_workspace_offset(dec, p) for p in parts]
+    assert all(o is not None and o % 256 == 0 for o in offs)
+    assert offs == sorted(offs) and offs[-1] < n
+    R = 256 * 8
+    assert offs[parts.index(moe.MOE_WS_H_LO)] - offs[parts.index(moe.MOE_WS_H)] >= (R + 256) * 1536 * 2
+    assert moe.moe_workspace_offset(dec, moe.MOE_WS_H_SCALES) is None
+    big = moe.make_config(T=16384, H=5120, E=256, S=1, k=8, I=1536)
+    assert moe.moe_workspace_offset(big, moe.MOE_WS_H_LO) is None
+    assert moe.moe_workspace_offset(big, moe.MOE_WS_H) is not None
+    f8 = moe.make_config(T=256, H=5120, E=256, S=1, k=8, I=1536, expert="fp8")
+    assert moe.moe_workspace_offset(f8, moe.MOE_WS_H_LO) is None
+    assert moe.moe_workspace_offset(f8, moe.MOE_WS_H_SCALES) is not None
+    s0 = moe.make_config(T=64, H=512, E=8, S=0, k=2, I=128)
+    assert moe.moe_workspace_offset(s0, moe.MOE_WS_Y_SHARED) is None
+    assert moe.moe_workspace_offset(dec, 11) is None and moe.moe_workspace_offset(dec, -1) is None
+    assert moe.moe_workspace_offset(moe.make_config(T=1, H=100, E=8, S=1, k=2, I=128),
+                                    moe.MOE_WS_H) is None

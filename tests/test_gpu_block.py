@@ -14,7 +14,8 @@ import torch
 
 import oracle
 from moe_inputs import config, generate
-from _gpu_helpers import assert_close, bf16_round, check_routing, log, out_to_f64, untied
+from _gpu_helpers import (assert_close, bf16_round, check_layer_output, check_routing,
+                          layer_routing, log, out_to_f64, tied_tokens, untied)
 
 pytestmark = pytest.mark.gpu
 
@@ -138,8 +139,8 @@ def test_grouped_layer_forward_small():
     lay = DeviceLayer(cfg, inp)
     out = lay.forward()
     torch.cuda.synchronize()
-    res = oracle.layer_forward(cfg, inp)
-    assert_close(cfg, out_to_f64(out), res.out, "grouped layer", mask=untied(res.routing))
+    idx, w = layer_routing(moe, lay)
+    check_layer_output(cfg, inp, out_to_f64(out), idx, "grouped layer", w_gpu=w)
 
 
 def test_grouping_arguments_are_checked():
@@ -180,19 +181,20 @@ def test_block_forward_small(case):
     lay = DeviceLayer(cfg, inp)
     g_st, g = gamma_for(cfg)
     out, counts, _ = _block(cfg, inp, lay, g_st)
-    ref, res = oracle.block_forward(cfg, inp, g)
-    ok = untied(res.routing)
-    assert_close(cfg, out_to_f64(out), ref, f"block {case}", mask=ok)
+    idx, w = layer_routing(moe, lay)
+    ref0, res0 = oracle.block_forward(cfg, inp, g)
+    check_routing(cfg, res0.routing, idx, w, f"block {case} routing")
+    # every token, against the oracle evaluated with the block's own choice
+    ref, res = oracle.block_forward(cfg, inp, g, idx=idx)
+    assert_close(cfg, out_to_f64(out), ref, f"block {case}")
     # the MoE part alone, against the layer output of the oracle
     h = oracle.widen(inp["x"], cfg.act)
     moe_part = out_to_f64(out) - h
     rnd = np.abs(ref) * (2.0 ** -8 if cfg.act == "bf16" else 2.0 ** -23)
-    err = np.abs(moe_part - res.out)[ok] - rnd[ok]
+    err = np.abs(moe_part - res.out) - rnd
     log(f"block {case}: MoE part max (|Δ| - output rounding)/rms = "
         f"{max(err.max(), 0) / oracle.rms(res.out):.3e}")
-    if ok.all():
-        np.testing.assert_array_equal(counts.cpu().numpy(),
-                                      np.bincount(res.routing.idx.ravel(), minlength=cfg.E))
+    np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(idx.ravel(), minlength=cfg.E))
     assert int(counts.sum()) == cfg.T * cfg.k
 
 
@@ -213,12 +215,14 @@ def test_block_forward_full_size_c2():
     g_st, g = gamma_for(cfg)
     log("block full C2: forward")
     out, counts, ties = _block(cfg, inp, lay, g_st)
-    tokens = np.sort(np.random.default_rng(202).choice(cfg.T, 128, replace=False))
-    tokens[0], tokens[-1] = 0, cfg.T - 1
-    ref, res = oracle.block_forward(cfg, inp, g, tokens=tokens)
-    ok = untied(res.routing)
-    log(f"block full C2: GPU ties {ties.cpu().tolist()}, oracle near-ties in sample {(~ok).sum()}")
-    assert_close(cfg, out_to_f64(out)[tokens], ref, "block full C2", mask=ok)
+    idx, w = layer_routing(moe, lay)
+    tokens = np.random.default_rng(202).choice(cfg.T, 128, replace=False)
+    tokens = np.union1d(tokens, [0, cfg.T - 1])
+    _, res0 = oracle.block_forward(cfg, inp, g, tokens=tokens)
+    check_routing(cfg, res0.routing, idx[tokens], w[tokens], "block full C2 routing")
+    ref, res = oracle.block_forward(cfg, inp, g, tokens=tokens, idx=idx[tokens])
+    log(f"block full C2: GPU ties {ties.cpu().tolist()}")
+    assert_close(cfg, out_to_f64(out)[tokens], ref, "block full C2")
     assert int(counts.sum()) == cfg.T * cfg.k
 
 

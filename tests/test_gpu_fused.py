@@ -12,7 +12,8 @@ import torch
 
 import oracle
 from moe_inputs import config, generate
-from _gpu_helpers import assert_close, log, out_to_f64, untied
+from _gpu_helpers import (assert_close, check_layer_output, layer_routing, log, out_to_f64,
+                          untied)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,12 +64,9 @@ def test_fused_matches_oracle(case):
     inp = generate(cfg)
     lay = DeviceLayer(cfg, inp)
     out, counts, ties = fused(lay)
-    res = oracle.layer_forward(cfg, inp)
-    ok = untied(res.routing)
-    assert_close(cfg, out_to_f64(out), res.out, f"fused {case}", mask=ok)
-    if ok.all():
-        np.testing.assert_array_equal(counts.cpu().numpy(),
-                                      np.bincount(res.routing.idx.ravel(), minlength=cfg.E))
+    idx, w = layer_routing(moe, lay)
+    check_layer_output(cfg, inp, out_to_f64(out), idx, f"fused {case}", w_gpu=w)
+    np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(idx.ravel(), minlength=cfg.E))
     assert int(counts.sum()) == cfg.T * cfg.k
     t = ties.cpu().numpy()
     assert t.min() >= 0 and t.max() <= cfg.T
@@ -81,17 +79,19 @@ def test_fused_full_size_c1_matches_oracle_and_layer():
     inp = generate(cfg)
     lay = DeviceLayer(cfg, inp)
     out, counts, _ = fused(lay)
-    ref_counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
-    ref = lay.forward(counts=ref_counts)
+    idx_f, w_f = layer_routing(moe, lay)
+    check_layer_output(cfg, inp, out_to_f64(out), idx_f, "fused full C1", w_gpu=w_f)
+    np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(idx_f.ravel(), minlength=cfg.E))
+    # against the multi-launch path: where both made the same choice of
+    # experts (they sum the router logits in different orders, so a near-tie
+    # may go either way), outputs within the same bar
+    ref = lay.forward()
     torch.cuda.synchronize()
-    res = oracle.layer_forward(cfg, inp)
-    ok = untied(res.routing)
-    log(f"fused full C1: oracle near-tie tokens {(~ok).sum()}")
-    assert_close(cfg, out_to_f64(out), res.out, "fused full C1", mask=ok)
-    # against the multi-launch path: the same routing away from near-ties,
-    # outputs within the same bar
-    np.testing.assert_array_equal(counts.cpu().numpy(), ref_counts.cpu().numpy())
-    assert_close(cfg, out_to_f64(out), out_to_f64(ref), "fused vs layer C1", mask=ok)
+    idx_l, _ = layer_routing(moe, lay)
+    same = np.all(idx_f == idx_l, axis=1)
+    log(f"fused full C1: {(~same).sum()} tokens chose differently from the multi-launch layer")
+    assert (~same).sum() <= 4
+    assert_close(cfg, out_to_f64(out), out_to_f64(ref), "fused vs layer C1", mask=same)
 
 
 def test_fused_rejects_other_regimes():

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from moe_inputs import config, generate
-from _gpu_helpers import assert_close, log, out_to_f64, untied
+from _gpu_helpers import check_layer_output, layer_routing, log, out_to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -35,17 +35,18 @@ def _need_gpu():
 
 def tiled_bytes(a: np.ndarray) -> np.ndarray:
     """[n, rows, cols] row-major -> the bytes of the tiled order: 16-row x
-    256-byte tiles, row group major, then along the row; rows of a tile
+    64-byte tiles, row group major, then along the row; rows of a tile
     contiguous inside it."""
     n, rows = a.shape[:2]
     b = np.ascontiguousarray(a).view(np.uint8).reshape(n, rows, -1)
     rb = b.shape[2]
-    t = b.reshape(n, rows // 16, 16, rb // 256, 256).transpose(0, 1, 3, 2, 4)
+    t = b.reshape(n, rows // 16, 16, rb // 64, 64).transpose(0, 1, 3, 2, 4)
     return np.ascontiguousarray(t).reshape(-1)
 
 
 @pytest.mark.parametrize("kind,shape", [("bf16", (3, 48, 384)), ("fp8", (2, 32, 512)),
                                         ("f32", (1, 16, 64)), ("bf16", (257, 32, 256)),
+                                        ("fp8", (3, 16, 64)), ("bf16", (2, 32, 96)),
                                         # > 2^24 chunks: the kernel's grid-stride loop wraps
                                         ("bf16", (40, 3072, 1280))])
 def test_pack_is_the_stated_permutation(kind, shape):
@@ -100,8 +101,8 @@ def test_layer_tiled_equals_row_major(case):
     b = tiled.forward()
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"{case}: layouts differ"
-    res = oracle.layer_forward(cfg, inp)
-    assert_close(cfg, out_to_f64(b), res.out, f"tiled layer {case}", mask=untied(res.routing))
+    idx, w = layer_routing(moe, tiled)
+    check_layer_output(cfg, inp, out_to_f64(b), idx, f"tiled layer {case}", w_gpu=w)
 
 
 @pytest.mark.parametrize("case", ["decode16", "S0"])
