@@ -25,8 +25,9 @@
  * Conventions for every entry point:
  *  - All tensor arguments are DEVICE pointers owned by the caller, row-major,
  *    16-byte aligned.  The library never allocates, frees, synchronises or
- *    copies to the host; it holds no mutable global state (only the
- *    thread-local text of the last HIP error, see moe_last_error_detail).
+ *    copies to the host; its only global state is the thread-local text of
+ *    the last HIP error (moe_last_error_detail) and the per-device scratch
+ *    array of moe_layer_forward_noalloc with its looked-up addresses.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
  *  - Arguments are validated on the host before anything is enqueued; on an
  *    error nothing is enqueued and no output is touched.  Launch failures
@@ -343,6 +344,24 @@ moe_status_t moe_layer_forward_timed(const moe_config_t* cfg, const moe_weights_
                                      int32_t* opt_tie_counts, void* workspace,
                                      size_t workspace_bytes, moe_stream_t stream,
                                      void* const* events);
+
+/* moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments otherwise, same launches
+ * and results as moe_layer_forward.  The workspace is a device array inside
+ * the library, MOE_NOALLOC_SCRATCH_BYTES (96 MiB) per GPU, held from the
+ * library's load on that GPU to the end of the process; configurations
+ * whose moe_workspace_size exceeds it return MOE_ERR_UNSUPPORTED and enqueue
+ * nothing (at the dots3 shapes -- H 5120, 256 + 1 experts, top-8, I 1536 --
+ * up to about 370 tokens).  The first call on a device looks up the array's
+ * device address (no allocation).  Every call on one GPU shares the array:
+ * calls that overlap in time on one GPU (other streams, other host threads)
+ * race and must be serialised by the caller; results of a finished call are
+ * in `out`, nothing needs to persist in the array between calls. */
+#define MOE_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
+moe_status_t moe_layer_forward_noalloc(const moe_config_t* cfg, const moe_weights_t* w,
+                                       const void* x, void* out, int32_t* opt_counts,
+                                       int32_t* opt_tie_counts, moe_stream_t stream);
 
 #ifdef __cplusplus
 }

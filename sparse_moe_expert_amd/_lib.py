@@ -28,7 +28,7 @@ EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_version", "moe_wor
            "moe_dispatch", "moe_grouped_ffn", "moe_expert_gate_up", "moe_expert_down",
            "moe_combine", "moe_quantize_fp8", "moe_layer_forward", "moe_layer_forward_timed",
            "moe_rmsnorm", "moe_block_forward", "moe_layer_forward_fused",
-           "moe_pack_expert_weights")
+           "moe_pack_expert_weights", "moe_layer_forward_noalloc")
 
 
 class MoEError(RuntimeError):
@@ -86,6 +86,7 @@ def _load():
         "moe_layer_forward_timed": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P, SZ, P,
                                                    ctypes.POINTER(ctypes.c_void_p)]),
         "moe_layer_forward_fused": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P, SZ, P]),
+        "moe_layer_forward_noalloc": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P]),
         "moe_rmsnorm": (ctypes.c_int, [CP, P, P, ctypes.c_float, P, P]),
         "moe_block_forward": (ctypes.c_int, [CP, WP, P, P, ctypes.c_float, P, I32P, I32P, P, SZ,
                                              P]),
@@ -242,6 +243,16 @@ def moe_layer_forward_fused(cfg, weights, x, out, opt_counts=None, opt_tie_count
     _check(LIB.moe_layer_forward_fused(ctypes.byref(cfg), ctypes.byref(weights), _ptr(x),
                                        _ptr(out), _ptr(opt_counts), _ptr(opt_tie_counts), wp, wb,
                                        _stream(stream)), "moe_layer_forward_fused")
+
+
+def moe_layer_forward_noalloc(cfg, weights, x, out, opt_counts=None, opt_tie_counts=None,
+                              stream=None):
+    _check(LIB.moe_layer_forward_noalloc(ctypes.byref(cfg), ctypes.byref(weights), _ptr(x),
+                                         _ptr(out), _ptr(opt_counts), _ptr(opt_tie_counts),
+                                         _stream(stream)), "moe_layer_forward_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 96 << 20
 
 
 def moe_rmsnorm(cfg, h, gamma, eps, out, stream=None):

@@ -8,8 +8,17 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 #include "moe_internal.h"
+
+// Device-resident workspace of moe_layer_forward_noalloc, for callers that
+// cannot allocate.  Each GPU holds its own copy from module load to process
+// end.  Host code never passes this name to a kernel: it is a host-side
+// stand-in; the device address comes from hipGetSymbolAddress, once per
+// device (moe::scratch_ptr below).
+constexpr size_t kScratchBytes = size_t{96} << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace moe {
 namespace {
@@ -317,6 +326,28 @@ GemmLaunch down_launch(const moe_config_t& c, const Layout& L, void* y_sorted, v
 hipError_t run_down(const moe_config_t& c, const Layout& L, void* y_sorted, void* y_shared,
                     void* ws, hipStream_t st) {
   return launch_gemm(expert_kind(c), K_F32, L.dn, down_launch(c, L, y_sorted, y_shared, ws), st);
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current and kept for the process.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -707,6 +738,22 @@ moe_status_t moe_block_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   if (e == hipSuccess)
     e = layer_run(c, w, xn, h, out, opt_counts, opt_tie_counts, workspace, st, nullptr);
   return hip_status(e);
+}
+
+moe_status_t moe_layer_forward_noalloc(const moe_config_t* cfg, const moe_weights_t* w,
+                                       const void* x, void* out, int32_t* opt_counts,
+                                       int32_t* opt_tie_counts, moe_stream_t stream) {
+  moe_status_t s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (make_layout(*cfg).total > kScratchBytes) return MOE_ERR_UNSUPPORTED;
+  if ((s = check_weights(*cfg, w, true, true)) != MOE_OK) return s;
+  if (cfg->T == 0) return MOE_OK;
+  void* ws = nullptr;
+  clear_stale_error();
+  if ((s = hip_status(scratch_ptr(&ws))) != MOE_OK) return s;
+  if ((s = check_layer_args(cfg, w, x, out, ws, kScratchBytes, nullptr)) != MOE_OK) return s;
+  return hip_status(layer_run(*cfg, w, x, nullptr, out, opt_counts, opt_tie_counts, ws,
+                              static_cast<hipStream_t>(stream), nullptr));
 }
 
 }  // extern "C"
