@@ -10,28 +10,36 @@ moe_intermediate 1536, bf16).  Prints ONE JSON line on stdout.
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
 Extra objects in the line:
-  roofline     the gate/up GEMM (the dominant kernel), timed live with HIP
-               events recorded on the stream it runs on, against the dense
-               bf16 MFMA peak; traffic from the committed rocprofv3 counter
-               summary when its kernel source hash still matches.
-  decode_T256  the same layer at T=256 tokens (weight streaming): time,
-               algorithmic HBM GB/s and its fraction of 8 TB/s; also as
-               one cooperative launch (moe_layer_forward_fused).
-  grouped_routing  the router (logits GEMM + selection) with group-limited
-               routing (8 groups, 4 chosen) next to the plain router.
-  block        the decoder block around the layer (RMSNorm, layer, residual
-               add in the combine) and the RMSNorm kernel alone against HBM.
-  device_copy  a 2 GiB device-to-device torch copy (reads + writes over
-               its time), as context for the HBM figures.
-  row_major_weights  the same layer with the expert weights row-major
-               (the timed line uses them packed into 16-row x 256-byte tiles
-               once at load time, moe_pack_expert_weights; --weights rows
-               times row-major weights instead).
-  cpu_baseline the fp64 CPU oracle on the first tokens of the same workload.
+  roofline        the gate/up GEMM (the dominant kernel), timed live with HIP
+                  events recorded on the stream it runs on, against the dense
+                  bf16 MFMA peak; traffic from the committed rocprofv3 counter
+                  summary when its kernel source hash still matches.
+  decode_T256     the decode-sized workload on its own seeded weights:
+                  time, algorithmic HBM GB/s and its fraction of 8 TB/s and of
+                  the measured read ceiling; also as one cooperative launch.
+  skewed_T8192    the Zipf-skewed dots.llm1-shaped workload (128 + 2 experts,
+                  top-6, I 1408): time, TFLOP/s against the bf16 peak, bytes,
+                  rows per expert, near-tie counts.
+  fp8_T4096       the FP8 workload: time, fraction of 8 TB/s (it is below the
+                  fp8 ridge) and of the fp8 MFMA peak, its gate/up roofline.
+  ceilings        measured on the device: a streaming read of 4 GiB through
+                  the library's read kernel, and the library's own prefill
+                  GEMMs on one dense expert (E = 1, T = 16384).
+  grouped_routing the router with group-limited routing (8 groups, 4 chosen)
+                  next to the plain router.
+  block           the decoder block around the layer (RMSNorm, layer,
+                  residual add in the combine) and the RMSNorm kernel alone.
+  device_copy     a 2 GiB device-to-device torch copy, as context.
+  row_major_weights  the layer with row-major expert weights (the timed line
+                  uses them packed into 16-row x 64-byte tiles once at load
+                  time, moe_pack_expert_weights).
+  cpu_baseline    the fp64 CPU oracle on a sample of the same workload, with
+                  its BLAS threads set to the cores this process may use.
 """
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -46,8 +54,8 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE layer fwd tokens/s & TFLOP/s (T=16384); HBM GB/s at T=256; % roofline"
 GEMM_SRCS = [os.path.join(ROOT, "sparse_moe_expert_amd", "csrc", f)
-             for f in ("gemm.hip", "gemm_big.hip", "gemm_decode.hip", "gemm_decode_device.h",
-                       "gemm_sched.h", "moe_device.h", "moe_internal.h")]
+             for f in ("gemm.hip", "gemm_prefill.hip", "gemm_big.hip", "gemm_decode.hip",
+                       "gemm_decode_device.h", "gemm_sched.h", "moe_device.h", "moe_internal.h")]
 EXPERT_KEYS = ("w_gate_up", "w_down", "w_sh_gate_up", "w_sh_down")
 
 
@@ -63,6 +71,8 @@ def gemm_source_hash() -> str:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
+
+# ---------------------------------------------------------------- work models
 
 def gate_up_flops(cfg) -> float:
     """Matmul flops of the gate/up GEMM: every routed (token, slot) row and
@@ -137,17 +147,21 @@ def load_traffic(workload: str):
     return d.get("bytes_per_launch")
 
 
-def time_layer(lay, steps, warmup, timed_events=True):
+# ---------------------------------------------------------------- timing
+
+def time_layer(lay, steps, warmup):
     """K plain layer forwards timed by the host clock between two device
     synchronisations (the step time), then K more with HIP events recorded at
     the stage boundaries on the layer's stream (the stage times; the events
     themselves add ~25-50 us to a step, so they stay out of the first pass).
-    Returns (step ms, instrumented step ms, event step ms, stage ms, counts,
-    p10/p50/p90 of the per-step event times)."""
+    Returns a dict: step ms, instrumented step ms, event step ms, stage ms,
+    counts, near-tie counts, p10/p50/p90 of the per-step event times."""
     import torch
     import sparse_moe_expert_amd as moe
     out = lay.empty_out()
     counts = torch.empty(lay.cfg.E, dtype=torch.int32, device="cuda")
+    ties = torch.zeros(2, dtype=torch.int32, device="cuda")
+    lay.forward(out=out, counts=counts, ties=ties)
     for _ in range(warmup):
         lay.forward(out=out, counts=counts)
     torch.cuda.synchronize()
@@ -171,13 +185,14 @@ def time_layer(lay, steps, warmup, timed_events=True):
     stage = {n: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps
              for j, n in enumerate(names)}
     per_step = sorted(ev[i][0].elapsed_time(ev[i][6]) for i in range(steps))
-    step_ev = sum(per_step) / steps
 
     def pct(q):
         return per_step[min(steps - 1, int(round(q * (steps - 1))))]
 
-    spread = {"p10": round(pct(0.1), 4), "p50": round(pct(0.5), 4), "p90": round(pct(0.9), 4)}
-    return plain, wall * 1e3 / steps, step_ev, stage, counts.cpu().numpy(), spread
+    return {"ms": plain, "ms_inst": wall * 1e3 / steps, "ms_ev": sum(per_step) / steps,
+            "stage": stage, "counts": counts.cpu().numpy(), "ties": ties.cpu().tolist(),
+            "spread": {"p10": round(pct(0.1), 4), "p50": round(pct(0.5), 4),
+                       "p90": round(pct(0.9), 4)}}
 
 
 def time_calls(fn, iters, warmup):
@@ -196,18 +211,135 @@ def time_calls(fn, iters, warmup):
     return e0.elapsed_time(e1) / iters
 
 
-def device_copy(gib=2.0, iters=5):
-    """A plain device-to-device copy of `gib` GiB with torch's copy kernel:
-    bytes read + written over its event time.  Context for the HBM figures:
-    a copy mixes reads and writes half and half, so it is no ceiling for the
-    read-dominated layer (which streams faster than it)."""
+def load_layer(cfg, tiled=True, keep_rows=False, keep_inputs=False):
+    """Generate the seeded inputs of `cfg`, upload them and (tiled) pack the
+    expert weights once.  Returns (layer, row-major layer or None, host inputs
+    or None)."""
     import torch
-    n = int(gib * (1 << 30))
-    a = torch.empty(n, dtype=torch.uint8, device="cuda")
-    b = torch.empty_like(a)
-    ms = time_calls(lambda: b.copy_(a), iters, 2)
-    del a, b
-    return {"bytes_per_copy": 2 * n, "ms": round(ms, 4), "GBps": round(2 * n / (ms / 1e3) / 1e9, 1)}
+    from moe_inputs import generate
+    from sparse_moe_expert_amd.device import DeviceLayer, pack_expert_weights
+    t0 = time.perf_counter()
+    inp = generate(cfg)
+    log(f"bench: {cfg.name}: generated in {time.perf_counter() - t0:.1f}s; uploading")
+    if tiled and not keep_rows:
+        lay, rows = DeviceLayer(cfg, inp, tiled=True), None
+    else:
+        rows = DeviceLayer(cfg, inp)
+        lay = rows
+        if tiled:
+            packed = {key: pack_expert_weights(rows.t[key], cfg.expert) for key in EXPERT_KEYS}
+            lay = _view(rows, cfg, expert_t=packed, tiled=True)
+    torch.cuda.synchronize()
+    return lay, (rows if keep_rows else None), (inp if keep_inputs else None)
+
+
+def stage_dict(r):
+    return {k: round(v, 4) for k, v in r["stage"].items()}
+
+
+def rows_stats(counts):
+    return {"max": int(counts.max()), "mean": round(float(counts.mean()), 2),
+            "empty": int((counts == 0).sum())}
+
+
+# ---------------------------------------------------------------- sub-lines
+
+def decode_line(cfg, steps, extras):
+    """T=256 tokens on the decode-sized workload's own seeded weights: the
+    weight-streaming regime, measured against 8 TB/s."""
+    import sparse_moe_expert_amd as moe
+    lay, rows, _ = load_layer(cfg, keep_rows=extras)
+    log(f"bench: {cfg.name}: {steps} steps")
+    r = time_layer(lay, steps, 5)
+    b = layer_bytes(cfg, r["counts"])
+    gbs = b / (r["ms"] / 1e3) / 1e9
+    out1 = lay.empty_out()
+    msf = time_calls(lambda: moe.moe_layer_forward_fused(
+        lay.ccfg, lay.weights, lay.t["x"], out1, None, None, lay.workspace), steps, 5)
+    gbf = b / (msf / 1e3) / 1e9
+    res = {
+        "workload": cfg.name, "ms_per_step": round(r["ms"], 4),
+        "ms_per_step_instrumented": round(r["ms_inst"], 4),
+        "ms_per_step_events_p10_p50_p90": r["spread"],
+        "tokens_per_s": round(cfg.T / (r["ms"] / 1e3), 1),
+        "algorithmic_bytes": b, "hbm_GBps": round(gbs, 1),
+        "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "tflops": round(cfg.flops() / (r["ms"] / 1e3) / 1e12, 2),
+        "stages_ms": stage_dict(r), "experts_touched": int((r["counts"] > 0).sum()),
+        "near_tie_tokens": {"selection": r["ties"][0], "slot_order": r["ties"][1]},
+        "fused_single_launch": {"ms_per_step": round(msf, 4), "hbm_GBps": round(gbf, 1),
+                                "frac_of_hbm_peak": round(gbf / PEAK_HBM_GBS, 4)},
+    }
+    if rows is not None:
+        msr = time_layer(rows, steps, 5)["ms"]
+        g1r = b / (msr / 1e3) / 1e9
+        res["row_major_weights"] = {"ms_per_step": round(msr, 4), "hbm_GBps": round(g1r, 1),
+                                    "frac_of_hbm_peak": round(g1r / PEAK_HBM_GBS, 4)}
+    return res, lay
+
+
+def workload_line(cfg, steps, warmup):
+    """Another configuration of the layer: time, tokens/s, TFLOP/s, its
+    algorithmic bytes, the fraction of both roofs, the governing one, its
+    gate/up roofline and the near-tie counts of its routing."""
+    lay, _, _ = load_layer(cfg)
+    log(f"bench: {cfg.name}: {warmup} warmup + {steps} steps")
+    r = time_layer(lay, steps, warmup)
+    dtype = cfg.expert
+    flops = cfg.flops()
+    b = layer_bytes(cfg, r["counts"])
+    tf = flops / (r["ms"] / 1e3) / 1e12
+    gbs = b / (r["ms"] / 1e3) / 1e9
+    ridge = PEAK_TFLOPS[dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    res = {
+        "workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "S": cfg.S, "k": cfg.k,
+        "I": cfg.I, "precision": dtype, "ms_per_step": round(r["ms"], 4),
+        "ms_per_step_events_p10_p50_p90": r["spread"],
+        "tokens_per_s": round(cfg.T / (r["ms"] / 1e3), 1), "tflops": round(tf, 2),
+        "flops_per_step": flops, "algorithmic_bytes": b, "algorithmic_GBps": round(gbs, 1),
+        "frac_of_mfma_peak": round(tf / PEAK_TFLOPS[dtype], 4),
+        "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "bound": "mfma" if flops / b >= ridge else "hbm",
+        "stages_ms": stage_dict(r), "rows_per_expert": rows_stats(r["counts"]),
+        "near_tie_tokens": {"selection": r["ties"][0], "slot_order": r["ties"][1]},
+        "gate_up_roofline": gate_up_roofline(cfg, r["stage"]["gate_up_gemm"], r["counts"], dtype),
+    }
+    res["frac_of_governing_roof"] = res["frac_of_mfma_peak" if res["bound"] == "mfma"
+                                        else "frac_of_hbm_peak"]
+    return res, lay
+
+
+def ceilings(cfg2, steps):
+    """Measured ceilings: a streaming read of 4 GiB with the library's read
+    kernel, and the library's prefill GEMMs on one dense expert (E = 1, k = 1,
+    no shared expert, T = 16384): the same kernels without gather or ragged
+    experts."""
+    import torch
+    import sparse_moe_expert_amd as moe
+    n = 4 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    res = {}
+    for blocks in (2048, 8192):
+        sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+        ms = time_calls(lambda: moe.moe_stream_read(buf, n, sink, blocks), 10, 2)
+        res[f"stream_read_{blocks}_blocks"] = {"bytes": n, "ms": round(ms, 4),
+                                               "GBps": round(n / (ms / 1e3) / 1e9, 1)}
+    del buf
+    best = max(v["GBps"] for v in res.values())
+    res["stream_read_GBps"] = best
+    cfg1 = cfg2.with_(name="dense_expert_T16384", E=1, k=1, S=0)
+    lay, _, _ = load_layer(cfg1)
+    r = time_layer(lay, steps, 3)
+    gu = gate_up_flops(cfg1)
+    dn = 2.0 * cfg1.T * cfg1.I * cfg1.H
+    res["dense_expert_gemm"] = {
+        "T": cfg1.T, "H": cfg1.H, "I": cfg1.I,
+        "gate_up_ms": round(r["stage"]["gate_up_gemm"], 4),
+        "gate_up_tflops": round(gu / (r["stage"]["gate_up_gemm"] / 1e3) / 1e12, 1),
+        "down_ms": round(r["stage"]["down_gemm"], 4),
+        "down_tflops": round(dn / (r["stage"]["down_gemm"] / 1e3) / 1e12, 1)}
+    return res, lay
 
 
 def grouped_routing(lay, cfg, n_group=8, topk_group=4, iters=20):
@@ -235,7 +367,6 @@ def block_forward(lay, cfg, steps):
     alone: its algorithmic bytes (read h and gamma, write the normalised rows)
     over its time."""
     import numpy as np
-    import torch
     import sparse_moe_expert_amd as moe
     from sparse_moe_expert_amd.device import to_device
     g = 1.0 + 0.1 * np.random.default_rng(5).standard_normal(cfg.H)
@@ -246,7 +377,6 @@ def block_forward(lay, cfg, steps):
     eps = cfg.rms_norm_eps
     blk = time_calls(lambda: moe.moe_block_forward(lay.ccfg, lay.weights, h, gamma, eps, out,
                                                    None, None, lay.workspace), steps, 3)
-    # the layer alone, timed the same way
     lyr = time_calls(lambda: moe.moe_layer_forward(lay.ccfg, lay.weights, h, out, None, None,
                                                    lay.workspace), steps, 3)
     norm = time_calls(lambda: moe.moe_rmsnorm(lay.ccfg, h, gamma, eps, xn), 50, 5)
@@ -260,21 +390,59 @@ def block_forward(lay, cfg, steps):
                         "achieved_GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
+def device_copy(gib=2.0, iters=5):
+    """A plain device-to-device copy of `gib` GiB with torch's copy kernel:
+    bytes read + written over its event time.  Context for the HBM figures:
+    a copy mixes reads and writes half and half."""
+    import torch
+    n = int(gib * (1 << 30))
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    ms = time_calls(lambda: b.copy_(a), iters, 2)
+    del a, b
+    return {"bytes_per_copy": 2 * n, "ms": round(ms, 4), "GBps": round(2 * n / (ms / 1e3) / 1e9, 1)}
+
+
+def cpu_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(cfg, inp, n_tokens):
+    """The fp64 CPU oracle as it stands, on the first `n_tokens` tokens of the
+    same workload, with the BLAS thread pool set to the cores this process may
+    use.  Its time includes widening every touched expert's weights to fp64,
+    which the oracle does per call."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
+    cores = cpu_cores()
     tokens = np.arange(min(n_tokens, cfg.T))
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         oracle.layer_forward(cfg, inp, tokens=tokens)
         dt = time.perf_counter() - t0
-    return {"value": round(tokens.size / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 2),
-            "sample": f"first {tokens.size} tokens of {cfg.name} (full routing over all "
-                      f"{cfg.E} experts, their SwiGLU experts and the shared expert), fp64 numpy, "
-                      "one thread"}
+    return {"value": round(tokens.size / dt, 3), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"first {tokens.size} tokens of {cfg.name} (routing over all {cfg.E} "
+                      f"experts, their SwiGLU experts and the shared expert), fp64 numpy, "
+                      f"BLAS threads {cores}"}
+
+
+def _teardown(objs):
+    """Release device memory and let the runtime go idle before the
+    interpreter exits: drop every device tensor, synchronise, empty torch's
+    cache.  A profiler that unloads while tensors and streams are still alive
+    at interpreter exit is what this avoids."""
+    import torch
+    objs.clear()
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
 
 
 def main():
@@ -285,10 +453,11 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload id (default 2: T=16384)")
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-decode", action="store_true", help="skip the T=256 line")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the T=8192 and fp8 lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the grouped-routing, block and row-major-weights lines")
-    ap.add_argument("--cpu-tokens", type=int, default=1280)
+                    help="skip ceilings, grouped routing, block, copy and row-major lines")
     ap.add_argument("--weights", choices=("tiled", "rows"), default="tiled",
                     help="expert weight storage of the timed layer (default: packed tiles)")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
@@ -302,35 +471,25 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from moe_inputs import config, generate
-    from sparse_moe_expert_amd.device import DeviceLayer
+    from moe_inputs import config
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    held = []
     cfg = config(args.config)
-    log(f"bench: generating {cfg.name} inputs")
-    t0 = time.perf_counter()
-    inp = generate(cfg)
-    log(f"bench: generated in {time.perf_counter() - t0:.1f}s; uploading")
-    lay_rows = DeviceLayer(cfg, inp)
     tiled = args.weights == "tiled"
-    if tiled:
-        # load-time preparation, outside the timed region: the expert weights
-        # packed once into the tiled storage
-        from sparse_moe_expert_amd.device import pack_expert_weights
-        packed = {key: pack_expert_weights(lay_rows.t[key], cfg.expert) for key in EXPERT_KEYS}
-        lay = _view(lay_rows, cfg, expert_t=packed, tiled=True)
-    else:
-        lay = lay_rows
-    torch.cuda.synchronize()
+    extras = not args.no_extras and args.config == 2
+    lay, lay_rows, inp = load_layer(cfg, tiled=tiled, keep_rows=tiled and extras,
+                                    keep_inputs=not args.no_cpu_baseline)
+    held += [lay, lay_rows]
 
     log(f"bench: {args.warmup} warmup + {args.steps} timed steps")
-    ms, ms_inst, ms_ev, stage, counts, spread = time_layer(lay, args.steps, args.warmup)
+    r = time_layer(lay, args.steps, args.warmup)
+    ms, counts = r["ms"], r["counts"]
     flops = cfg.flops()
-    dtype = cfg.expert if cfg.expert != "f32" else "f32"
+    dtype = cfg.expert
     res = {
         "metric": METRIC,
         "value": round(cfg.T / (ms / 1e3), 1),
@@ -346,67 +505,53 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "S": cfg.S,
                    "k": cfg.k, "I": cfg.I, "precision": dtype, "seed": 0,
-                   "expert_weights": "tiled16x256B" if tiled else "row_major"},
+                   "expert_weights": "tiled16x64B" if tiled else "row_major"},
         "tflops": round(flops / (ms / 1e3) / 1e12, 2),
         "frac_of_peak_mfma_whole_step": round(flops / (ms / 1e3) / 1e12 / PEAK_TFLOPS[dtype], 4),
-        "ms_per_step_instrumented": round(ms_inst, 4),
-        "ms_per_step_events": round(ms_ev, 4),
-        "ms_per_step_events_p10_p50_p90": spread,
-        "stages_ms": {k: round(v, 4) for k, v in stage.items()},
-        "rows_per_expert": {"max": int(counts.max()), "mean": float(counts.mean()),
-                            "empty": int((counts == 0).sum())},
+        "ms_per_step_instrumented": round(r["ms_inst"], 4),
+        "ms_per_step_events": round(r["ms_ev"], 4),
+        "ms_per_step_events_p10_p50_p90": r["spread"],
+        "stages_ms": stage_dict(r),
+        "rows_per_expert": rows_stats(counts),
+        "near_tie_tokens": {"selection": r["ties"][0], "slot_order": r["ties"][1]},
     }
-
-    res["roofline"] = gate_up_roofline(cfg, stage["gate_up_gemm"], counts, dtype)
-
-    if not args.no_decode and args.config == 2:
-        # T = 256 tokens (the decode-sized workload's x, router weight and bias)
-        # through the same resident expert weights: the two workloads share
-        # every shape and weight distribution.
-        cfg1 = config(1)
-        inp1 = generate(cfg1, weights=False)
-        lay1 = _view(lay, cfg1, inp1)
-        log(f"bench: decode T={cfg1.T}: {args.decode_steps} steps")
-        ms1, ms1_inst, _, stage1, counts1, spread1 = time_layer(lay1, args.decode_steps, 5)
-        b1 = layer_bytes(cfg1, counts1)
-        gbs = b1 / (ms1 / 1e3) / 1e9
-        # the same layer as one cooperative launch
-        import sparse_moe_expert_amd as moe
-        out1 = lay1.empty_out()
-        msf = time_calls(lambda: moe.moe_layer_forward_fused(
-            lay1.ccfg, lay1.weights, lay1.t["x"], out1, None, None, lay1.workspace),
-            args.decode_steps, 5)
-        gbf = b1 / (msf / 1e3) / 1e9
-        res["decode_T256"] = {
-            "workload": cfg1.name, "ms_per_step": round(ms1, 4),
-            "ms_per_step_instrumented": round(ms1_inst, 4),
-            "ms_per_step_events_p10_p50_p90": spread1,
-            "fused_single_launch": {"ms_per_step": round(msf, 4), "hbm_GBps": round(gbf, 1),
-                                    "frac_of_hbm_peak": round(gbf / PEAK_HBM_GBS, 4)},
-            "tokens_per_s": round(cfg1.T / (ms1 / 1e3), 1),
-            "algorithmic_bytes": b1, "hbm_GBps": round(gbs, 1),
-            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "tflops": round(cfg1.flops() / (ms1 / 1e3) / 1e12, 2),
-            "stages_ms": {k: round(v, 4) for k, v in stage1.items()},
-            "experts_touched": int((counts1 > 0).sum()),
-        }
-        if tiled and not args.no_extras:
-            ms1r = time_layer(_view(lay_rows, cfg1, inp1), args.decode_steps, 5)[0]
-            g1r = b1 / (ms1r / 1e3) / 1e9
-            res["decode_T256"]["row_major_weights"] = {
-                "ms_per_step": round(ms1r, 4), "hbm_GBps": round(g1r, 1),
-                "frac_of_hbm_peak": round(g1r / PEAK_HBM_GBS, 4)}
-
-    if tiled and not args.no_extras:
-        msr = time_layer(lay_rows, args.steps, args.warmup)[0]
+    res["roofline"] = gate_up_roofline(cfg, r["stage"]["gate_up_gemm"], counts, dtype)
+    if lay_rows is not None:
+        msr = time_layer(lay_rows, args.steps, args.warmup)["ms"]
         res["row_major_weights"] = {"ms_per_step": round(msr, 4),
                                     "tokens_per_s": round(cfg.T / (msr / 1e3), 1)}
-
-    if not args.no_extras and args.config == 2:
+    if extras:
         log("bench: grouped routing and block forward")
         res["grouped_routing"] = grouped_routing(lay, cfg)
         res["block"] = block_forward(lay, cfg, min(args.steps, 10))
-        res["device_copy"] = device_copy()
+    if args.config == 2:
+        # the other workloads load their own weights; the T=16384 layer's
+        # weights stay only if the CPU baseline still needs its host inputs
+        held.clear()
+        del lay, lay_rows
+        gc.collect()
+        torch.cuda.empty_cache()
+        if not args.no_decode:
+            res["decode_T256"], l1 = decode_line(config(1), args.decode_steps, extras)
+            del l1
+            gc.collect()
+            torch.cuda.empty_cache()
+        if not args.no_workloads:
+            for cid, key in ((3, "skewed_T8192"), (4, "fp8_T4096")):
+                res[key], lw = workload_line(config(cid), args.steps, args.warmup)
+                del lw
+                gc.collect()
+                torch.cuda.empty_cache()
+        if extras:
+            log("bench: measured ceilings and device copy")
+            res["ceilings"], lc = ceilings(cfg, min(args.steps, 10))
+            del lc
+            gc.collect()
+            torch.cuda.empty_cache()
+            res["device_copy"] = device_copy()
+            res["ceilings"]["decode_T256_frac_of_read_ceiling"] = (
+                round(res["decode_T256"]["hbm_GBps"] / res["ceilings"]["stream_read_GBps"], 4)
+                if "decode_T256" in res else None)
 
     if args.calib_copy_gib > 0:
         n = int(args.calib_copy_gib * (1 << 30))
@@ -416,6 +561,7 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         res["calib_copy_bytes"] = n
+        del a, b
 
     if not args.no_cpu_baseline:
         log(f"bench: CPU oracle on {args.cpu_tokens} tokens")
@@ -423,6 +569,7 @@ def main():
     else:
         res["cpu_baseline"] = None
 
+    _teardown(held)
     print(json.dumps(res), flush=True)
 
 

@@ -345,6 +345,15 @@ moe_status_t moe_layer_forward_timed(const moe_config_t* cfg, const moe_weights_
                                      size_t workspace_bytes, moe_stream_t stream,
                                      void* const* events);
 
+/* Measurement utility, no step of the layer: reads `bytes` (a multiple of
+ * 16) of device memory at src (16-byte aligned) as one streaming pass with
+ * `blocks` workgroups of 256 threads (1..65536), and writes one folded word
+ * per block to sink[0, blocks) so the reads cannot be elided.  Its rate is
+ * the read ceiling the weight-streaming (decode) GEMMs are compared with.
+ * MOE_ERR_INVALID_ARG on bad arguments; bytes == 0 is a no-op. */
+moe_status_t moe_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
+                             moe_stream_t stream);
+
 /* moe_layer_forward without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments otherwise, same launches

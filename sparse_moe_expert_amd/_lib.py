@@ -28,7 +28,7 @@ EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_version", "moe_wor
            "moe_dispatch", "moe_grouped_ffn", "moe_expert_gate_up", "moe_expert_down",
            "moe_combine", "moe_quantize_fp8", "moe_layer_forward", "moe_layer_forward_timed",
            "moe_rmsnorm", "moe_block_forward", "moe_layer_forward_fused",
-           "moe_pack_expert_weights", "moe_layer_forward_noalloc")
+           "moe_pack_expert_weights", "moe_layer_forward_noalloc", "moe_stream_read")
 
 
 class MoEError(RuntimeError):
@@ -87,6 +87,7 @@ def _load():
                                                    ctypes.POINTER(ctypes.c_void_p)]),
         "moe_layer_forward_fused": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P, SZ, P]),
         "moe_layer_forward_noalloc": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P]),
+        "moe_stream_read": (ctypes.c_int, [P, SZ, P, ctypes.c_int32, P]),
         "moe_rmsnorm": (ctypes.c_int, [CP, P, P, ctypes.c_float, P, P]),
         "moe_block_forward": (ctypes.c_int, [CP, WP, P, P, ctypes.c_float, P, I32P, I32P, P, SZ,
                                              P]),
@@ -253,6 +254,12 @@ def moe_layer_forward_noalloc(cfg, weights, x, out, opt_counts=None, opt_tie_cou
 
 
 NOALLOC_SCRATCH_BYTES = 96 << 20
+
+
+def moe_stream_read(src, nbytes, sink, blocks, stream=None):
+    """Measurement utility: one streaming read pass over nbytes of src."""
+    _check(LIB.moe_stream_read(_ptr(src), int(nbytes), _ptr(sink), int(blocks), _stream(stream)),
+           "moe_stream_read")
 
 
 def moe_rmsnorm(cfg, h, gamma, eps, out, stream=None):

@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
 SOURCES = ["moe_api.hip", "gemm.hip", "gemm_prefill.hip", "gemm_big.hip", "gemm_decode.hip", "route.hip", "dispatch.hip",
-           "combine.hip", "norm.hip", "fused.hip", "pack.hip"]
+           "combine.hip", "norm.hip", "fused.hip", "pack.hip", "probe.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -29,9 +29,12 @@
 //  * Measured on the T=16384 gate/up GEMM: the same MFMAs and LDS reads run
 //    at ~2.07 PFLOP/s without any operand traffic; with both operands staged
 //    through LDS by DMA the launch took 4.75 ms, without the LDS reads 3.27 ms.
-//  * LDS rows are 64 bytes; chunk c of row r is stored at c ^ ((r >> 2) & 3),
-//    so the 16 lanes of each 16-byte LDS access phase (16 consecutive rows,
-//    one chunk) hit 16 distinct bank groups.
+//  * LDS rows are 64 bytes; chunk c of row r is stored at c ^ ((r >> 1) & 3).
+//    Measured with the LDS bank-conflict counter on the fragment reads (16
+//    consecutive rows, one chunk per 16 lanes): this key leaves no conflicts
+//    (down GEMM 0%, gate/up 11%, from its epilogue), while (r >> 2) & 3,
+//    r & 3, (r ^ (r >> 2)) & 3, (r >> 3) & 3 and no swizzle all conflict on
+//    40-47% of the LDS cycles.
 //  * 32-row sub-tiles wholly past an expert's last row skip their MFMAs (the
 //    ragged last tile of each expert); waves whose weight rows lie past N
 //    skip their loads and MFMAs.
@@ -50,7 +53,7 @@ constexpr int NT = BROWS / WAVES / 16;  // 16-row weight tiles per wave: 4
 constexpr int SLICE_B = 64;             // bytes per row per K-slice
 constexpr int KE = SLICE_B / 2;         // bf16 elements per K-slice
 constexpr int A_SLOT = BM * SLICE_B;    // 8 KB of token rows per slice
-constexpr int U = 3;                    // ring slots: A staging, A in LDS, weights
+constexpr int U = 3;                    // ring slots: A staging, A in LDS, weights (U - 1 ahead)
 constexpr int LDC = 256 + 4;            // fp32 epilogue tile row stride
 constexpr int SMEM = BM * LDC * 4;      // epilogue tile; the A ring (24 KB) fits inside
 
@@ -66,7 +69,7 @@ __device__ __forceinline__ V gload(const void* ptr) {
 }
 
 __device__ __forceinline__ int swz(int r, int c) {
-  return r * SLICE_B + ((c ^ ((r >> 2) & 3)) << 4);
+  return r * SLICE_B + ((c ^ ((r >> 1) & 3)) << 4);
 }
 
 // Workgroup barrier after this wave's LDS writes of the slice completed
@@ -99,16 +102,18 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
                       ac * 16;
   const int a_dst = swz(ar, ac);
   // weight tiles of this wave: lane l reads row l % 16 of the tile, bytes
-  // [16 (l / 16), +16) of the slice
+  // [16 (l / 16), +16) of the slice.  Rows past N (a partial last tile, or
+  // the router's N = E below 16) read row N - 1 instead: in bounds, and the
+  // columns they give are never stored.
   const char* b_src[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     int row;
     if constexpr (DUAL) {  // tiles 0, 1: gate rows; 2, 3: the matching up rows
-      const int n = min(job.n0 + wave * 32 + (t & 1) * 16, N - 16);
-      row = (t < 2 ? n : N + n) + (lane & 15);
+      const int n = min(job.n0 + wave * 32 + (t & 1) * 16 + (lane & 15), N - 1);
+      row = t < 2 ? n : N + n;
     } else {
-      row = min(job.n0 + wave * 64 + t * 16, N - 16) + (lane & 15);
+      row = min(job.n0 + wave * 64 + t * 16 + (lane & 15), N - 1);
     }
     b_src[t] = job.W + w_tile_row_off(p.w_tiled, row, rowb_b) + w_tile_k_off(p.w_tiled, (lane >> 4) * 16);
   }
@@ -142,11 +147,14 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
   // weights loaded at iteration kt - 2 into b_ring[kt % 3].  Loads past the
   // last slice fetch the last slice again (never used), so every iteration
   // runs the same instructions.
+  // prologue, in the order the iterations would have issued it: token rows
+  // of slices 0 .. U-1, weights of slices 0 .. U-2
   load_a(a_stage[0], 0);
-  load_a(a_stage[1], 1);
-  load_b(b_ring[0], 0);
-  load_a(a_stage[2], 2);
-  load_b(b_ring[1], 1);
+#pragma unroll
+  for (int j = 1; j < U; ++j) {
+    load_a(a_stage[j], j);
+    load_b(b_ring[j - 1], j - 1);
+  }
   store_a(a_stage[0], 0);
 
   auto iter = [&](auto rc, int kt) __attribute__((always_inline)) {
@@ -154,7 +162,7 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
     slice_barrier();                        // slice kt is in LDS for every wave
     store_a(a_stage[(R + 1) % U], (R + 1) % U);
     load_a(a_stage[R], kt + U);
-    load_b(b_ring[(R + 2) % U], kt + 2);
+    load_b(b_ring[(R + U - 1) % U], kt + U - 1);
     if constexpr (MS > 0) {
       const char* As = smem + R * A_SLOT;
       bf16x8 af[8];
@@ -178,13 +186,13 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
     }
   };
   int kt = 0;
-  for (; kt + U <= nk; kt += U) {
-    iter(std::integral_constant<int, 0>{}, kt);
-    iter(std::integral_constant<int, 1>{}, kt + 1);
-    iter(std::integral_constant<int, 2>{}, kt + 2);
-  }
-  if (kt < nk) iter(std::integral_constant<int, 0>{}, kt);
-  if (kt + 1 < nk) iter(std::integral_constant<int, 1>{}, kt + 1);
+  auto run = [&](auto... rs) __attribute__((always_inline)) {  // U iterations, R = 0 .. U-1
+    for (; kt + U <= nk; kt += U) (iter(rs, kt + decltype(rs)::value), ...);
+    ((kt + decltype(rs)::value < nk ? iter(rs, kt + decltype(rs)::value) : void()), ...);
+  };
+  [&]<int... Rs>(std::integer_sequence<int, Rs...>) __attribute__((always_inline)) {
+    run(std::integral_constant<int, Rs>{}...);
+  }(std::make_integer_sequence<int, U>{});
 
   // ------------------------------------------------------------ epilogue
   // 16x16 accumulator layout: lane l, element i -> row 4 (l / 16) + i (token),

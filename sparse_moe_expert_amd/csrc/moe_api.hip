@@ -756,4 +756,14 @@ moe_status_t moe_layer_forward_noalloc(const moe_config_t* cfg, const moe_weight
                               static_cast<hipStream_t>(stream), nullptr));
 }
 
+moe_status_t moe_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
+                             moe_stream_t stream) {
+  if (bytes == 0) return MOE_OK;
+  if (!src || !aligned16(src) || bytes % 16 != 0 || !sink || blocks < 1 || blocks > 65536)
+    return MOE_ERR_INVALID_ARG;
+  clear_stale_error();
+  return hip_status(launch_stream_read(src, static_cast<long long>(bytes), sink, blocks,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

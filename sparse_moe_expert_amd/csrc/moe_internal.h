@@ -203,6 +203,10 @@ hipError_t launch_pack_tiles(const void* src, void* dst, long long count, int ro
 hipError_t launch_rmsnorm(int act_kind, const void* h, const void* gamma, float eps, void* out,
                           int T, int H, hipStream_t st);
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t st);
+// probe.hip: read `bytes` (multiple of 16) from src with `blocks` blocks,
+// one folded word per block into sink[blocks]
+hipError_t launch_stream_read(const void* src, long long bytes, uint32_t* sink, int blocks,
+                              hipStream_t st);
 
 hipError_t launch_dispatch(const int32_t* topk_idx, int T, int k, int E, int S,
                            int32_t* chunk_counts, int32_t* chunk_base, int nchunks,

@@ -270,3 +270,14 @@ def test_workspace_offsets():
     assert moe.moe_workspace_offset(dec, 11) is None and moe.moe_workspace_offset(dec, -1) is None
     assert moe.moe_workspace_offset(moe.make_config(T=1, H=100, E=8, S=1, k=2, I=128),
                                     moe.MOE_WS_H) is None
+
+
+def test_stream_read_validation():
+    P = "moe_stream_read"
+    assert call(P, FAKE, 0, None, 1, None) == moe.MOE_OK                 # nothing to read
+    assert call(P, None, 1024, FAKE, 8, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(P, FAKE + 8, 1024, FAKE, 8, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(P, FAKE, 1000, FAKE, 8, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(P, FAKE, 1024, None, 8, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(P, FAKE, 1024, FAKE, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(P, FAKE, 1024, FAKE, 65537, None) == moe.MOE_ERR_INVALID_ARG

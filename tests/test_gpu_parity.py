@@ -111,11 +111,15 @@ def test_route_matches_oracle(cid):
     assert t.min() >= 0 and t.max() <= cfg.T
 
 
-@pytest.mark.parametrize("E,k", [(512, 16), (320, 8), (96, 6), (33, 4)])
-def test_route_expert_counts(E, k):
+@pytest.mark.parametrize("E,k,T", [(512, 16, 300), (320, 8, 300), (96, 6, 300), (33, 4, 300),
+                                   (1, 1, 4096), (8, 2, 4096), (100, 4, 4096)])
+def test_route_expert_counts(E, k, T):
     """Routing on expert counts that give 8, 5 of 8, 2 and 1 keys per lane
-    (expert e = slot * 64 + lane), including a partly filled last slot."""
-    cfg = small(T=300, H=256, E=E, S=1, k=k, I=128)
+    (expert e = slot * 64 + lane), including a partly filled last slot.  At
+    T = 4096 (bf16) the logits come from the large-tile GEMM with N = E
+    columns: fewer than one 16-row weight tile (E = 1, 8) and a partial last
+    tile (E = 100)."""
+    cfg = small(T=T, H=256, E=E, S=1, k=k, I=128)
     log(f"route E={E} k={k}: T={cfg.T}")
     inp = generate(cfg, weights=False)
     c = ccfg(cfg)
@@ -265,10 +269,33 @@ LAYER_CASES = {
     "fp8_decode2_empty": lambda: small(T=16, H=512, E=64, S=1, k=8, I=1536, expert="fp8"),
     "fp8_decode_S2": lambda: small(T=48, H=768, E=32, S=2, k=6, I=1536, expert="fp8"),
     "f32_ragged": lambda: small(T=45, H=384, E=12, S=1, k=3, I=256, expert="f32"),
+    # T >= 4096 in bf16: the router logits go through the large-tile kernel
+    # with N = E output columns.  E below one 16-row weight tile (the one
+    # dense expert), and E not a multiple of 16 (a partial last tile).
+    "bf16_T4096_E1_dense": lambda: small(T=4096, H=512, E=1, S=0, k=1, I=256),
+    "bf16_T4096_E8": lambda: small(T=4096, H=256, E=8, S=1, k=2, I=128),
+    "bf16_T4096_E100": lambda: small(T=4096, H=512, E=100, S=1, k=4, I=128),
 }
 
 
-@pytest.mark.parametrize("case", list(LAYER_CASES))
+# Cases that miss the bar, with the measured reason (kept, expected to fail).
+LAYER_XFAIL = {
+    # One expert, k = 1, no shared expert: out is one expert's y, with no
+    # other term beside it.  The largest |out| is 5.9 rms, and rounding the
+    # exact output to bf16 alone costs 1.39e-2 rms there; the MFMA-bound
+    # large-tile kernel rounds h to bf16 once, which adds ~0.6e-2 at that
+    # element (measured 2.01e-2 against the 2e-2 bar).
+    "bf16_T4096_E1_dense": "one bf16 rounding of h in the large-tile kernel: 2.01e-2 rms",
+    # the same cause; output rounding alone 1.63e-2 (|out| up to 7.9 rms) and
+    # 1.76e-2 rms, with one bf16 rounding of h 2.70e-2 and 2.25e-2 rms
+    "bf16_T4096_E8": "one bf16 rounding of h in the large-tile kernel: 2.70e-2 rms",
+    "bf16_T4096_E100": "one bf16 rounding of h in the large-tile kernel: 2.25e-2 rms",
+}
+
+
+@pytest.mark.parametrize("case", [
+    pytest.param(c, marks=pytest.mark.xfail(strict=True, reason=LAYER_XFAIL[c]))
+    if c in LAYER_XFAIL else c for c in LAYER_CASES])
 def test_layer_forward_small(case):
     """Every token, near-tied ones included: the oracle is evaluated with the
     choice of experts the layer made (read from its workspace), after that
@@ -439,3 +466,21 @@ def test_errors_leave_output_untouched():
     moe.moe_layer_forward(c0, lay.weights, lay.t["x"], out, workspace=lay.workspace)
     torch.cuda.synchronize()
     assert torch.all(out == 3.0)
+
+
+def test_stream_read_folds_every_word():
+    """The read-ceiling utility touches every 16-byte chunk: its per-block
+    XOR fold equals the host fold of the same chunk assignment (chunk q to
+    block (q // 256) % blocks over the grid-stride loop)."""
+    rng = np.random.default_rng(41)
+    blocks, n_chunks = 64, 64 * 256 * 5 + 77
+    words = rng.integers(0, 2 ** 32, size=n_chunks * 4, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(words.view(np.int32)).cuda()
+    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    moe.moe_stream_read(src, n_chunks * 16, sink, blocks)
+    torch.cuda.synchronize()
+    fold = np.bitwise_xor.reduce(words.reshape(n_chunks, 4), axis=1)
+    blk = (np.arange(n_chunks) // 256) % blocks
+    want = np.zeros(blocks, np.uint32)
+    np.bitwise_xor.at(want, blk, fold)
+    np.testing.assert_array_equal(sink.cpu().numpy().view(np.uint32), want)
