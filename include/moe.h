@@ -82,7 +82,8 @@ typedef struct moe_config {
   int32_t I;        /* moe_intermediate_size of a routed expert; mult. of 128;
                        FP8 experts: at least 512, else MOE_ERR_UNSUPPORTED
                        (with fewer channels one e4m3 code of h that rounds
-                       the other way at a boundary moves y too much)       */
+                       the other way at a boundary moves y too much); bf16
+                       experts: at most 16384                              */
   int32_t I_shared; /* intermediate size of a shared expert; must equal I   */
   int32_t norm_topk_prob;      /* 1: renormalise the k chosen scores        */
   float routed_scaling_factor; /* multiplies the routing weights            */
@@ -177,12 +178,20 @@ size_t moe_workspace_size(const moe_config_t* cfg);
  *  MOE_WS_H          [T*k + S*T, I]    h = SiLU(W_g x) * (W_u x) per sorted row
  *                                      (routed rows first, then shared expert s
  *                                      token t at row T*k + s*T + t): bf16, fp32
- *                                      (MOE_F32 experts) or e4m3 codes (FP8)
+ *                                      (MOE_F32 experts) or e4m3 codes (FP8);
+ *                                      bf16 experts on the large-tile path:
+ *                                      fp16 codes c, h = c * 2^e (MOE_WS_H_EXP)
  *  MOE_WS_H_SCALES   fp32  [T*k + S*T, I/128]  FP8 only: h = code * scale
  *  MOE_WS_H_LO       bf16  [T*k + S*T, I]  bf16 experts on the weight-streaming
  *                                      and mid-size paths only: h - bf16(h),
  *                                      rounded to bf16 (h enters the down GEMM
  *                                      as MOE_WS_H + MOE_WS_H_LO)
+ *  MOE_WS_H_EXP      int32 [T*k + S*T, ceil(I/256)]  bf16 experts on the
+ *                                      large-tile path only: the exponent e of
+ *                                      each row and block of 256 h columns,
+ *                                      chosen so that the block's largest |c|
+ *                                      lies in [2^14, 2^15) (e = 0 for a block
+ *                                      of zeros)
  *  MOE_WS_Y          fp32  [T*k, H]    routed expert outputs, sorted rows
  *  MOE_WS_Y_SHARED   fp32  [S, T, H]   shared expert outputs
  * Returns the byte offset of `part` inside the workspace of
@@ -193,7 +202,7 @@ size_t moe_workspace_size(const moe_config_t* cfg);
 typedef enum {
   MOE_WS_TOPK_IDX = 0, MOE_WS_TOPK_W = 1, MOE_WS_COUNTS = 2, MOE_WS_OFFSETS = 3,
   MOE_WS_PERM = 4, MOE_WS_INV = 5, MOE_WS_H = 6, MOE_WS_H_SCALES = 7, MOE_WS_H_LO = 8,
-  MOE_WS_Y = 9, MOE_WS_Y_SHARED = 10
+  MOE_WS_Y = 9, MOE_WS_Y_SHARED = 10, MOE_WS_H_EXP = 11
 } moe_ws_part_t;
 size_t moe_workspace_offset(const moe_config_t* cfg, int32_t part);
 
@@ -239,10 +248,13 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx, int3
  * and for every shared expert s and token t:
  *   y_shared[s, t] = Wd_s (SiLU(Wg_s x_t) * (Wu_s x_t))   fp32 [S, T, H]
  * fp32 accumulation (SiLU in fp32 with the hardware exponential and
- * reciprocal); between the two GEMMs h is stored in bf16 -- as two bf16 terms
- * (h and its residue, ~16 significant bits) where the down GEMM streams its
- * weights (fewer than ~96 rows per expert), as one term on the large-tile
- * prefill path -- see MOE_WS_H_LO; y stays fp32 so that the layer output is
+ * reciprocal); between the two GEMMs h is stored as two bf16 terms (h and its
+ * residue, ~16 significant bits) where the down GEMM streams its weights
+ * (fewer than ~96 rows per expert; MOE_WS_H_LO), and on the MFMA-bound
+ * large-tile prefill path as fp16 scaled by a power of two per row and 256
+ * columns (11 significant bits; MOE_WS_H_EXP), where the down GEMM takes the
+ * bf16 weights as fp16 (exact within fp16's normal range, |w| >= 2^-14;
+ * smaller weights keep an absolute error below 2^-25); y stays fp32 so that the layer output is
  * rounded only once, in moe_combine.  FP8: x and h are quantised per token per 128 channels to e4m3
  * with scale amax/448 (fp32, see moe_quantize_fp8) before their GEMM; weights
  * use their block scales.  perm and offsets are moe_dispatch outputs (device).

@@ -19,7 +19,7 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 # moe_ws_part_t
 (MOE_WS_TOPK_IDX, MOE_WS_TOPK_W, MOE_WS_COUNTS, MOE_WS_OFFSETS, MOE_WS_PERM, MOE_WS_INV,
- MOE_WS_H, MOE_WS_H_SCALES, MOE_WS_H_LO, MOE_WS_Y, MOE_WS_Y_SHARED) = range(11)
+ MOE_WS_H, MOE_WS_H_SCALES, MOE_WS_H_LO, MOE_WS_Y, MOE_WS_Y_SHARED, MOE_WS_H_EXP) = range(12)
 WS_NONE = (1 << 64) - 1
 
 # every entry point of include/moe.h

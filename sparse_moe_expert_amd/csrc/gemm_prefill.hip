@@ -81,11 +81,43 @@ __device__ __forceinline__ void slice_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// 2^-sh as two fp16 (sh >= 0; 0 past fp16's smallest subnormal 2^-24).
+__device__ __forceinline__ half2v pow2_neg_f16x2(int sh) {
+  const uint32_t b = sh <= 14 ? static_cast<uint32_t>(15 - sh) << 10
+                              : (sh <= 24 ? 1u << (24 - sh) : 0u);
+  return __builtin_bit_cast(half2v, b | (b << 16));
+}
+
+// 8 bf16 -> 8 fp16: exact for |w| in fp16's normal range [2^-14, 65504];
+// smaller magnitudes round toward zero to a multiple of 2^-24, larger ones
+// saturate at 65504.
+__device__ __forceinline__ half8 bf16x8_to_f16(const bf16x8& w) {
+  const uint4 u = __builtin_bit_cast(uint4, w);
+  const uint32_t d[4] = {u.x, u.y, u.z, u.w};
+  half8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(d[i] << 16),
+                                              __uint_as_float(d[i] & 0xffff0000u));
+    r[2 * i] = h[0];
+    r[2 * i + 1] = h[1];
+  }
+  return r;
+}
+
 // One tile for a wave that computes MS 16-row sub-tiles (an even number up
 // to 8; 0: its weight rows lie past N, it only stages token rows).
-template <bool DUAL, int MS>
+// F16 (scaled fp16 h): the gate/up GEMM (DUAL) writes h as fp16 codes and
+// block exponents (c_exp); the projection reads A that way (a_exp), brings
+// each row's blocks to the row's largest exponent while staging them, runs
+// fp16 MFMAs with the bf16 weights converted in registers, and scales the
+// row by 2^e in its epilogue.  erow: BM ints of LDS outside smem.
+template <bool DUAL, int MS, bool F16>
 __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, char* smem, int nk,
-                                          int kt0) {
+                                          int kt0, int* erow) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -101,6 +133,28 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
                       gemm_a_source_row(p, job.row_begin + job.m0 + min(ar, job.rows_here - 1)) * rowb_a +
                       ac * 16;
   const int a_dst = swz(ar, ac);
+  // F16 projection: per staging row and block, the fp16 pair 2^-(e_row - e)
+  // that brings the block to the row's largest exponent e_row (LDS after the
+  // A ring; each slice reads its block's entry before the slice barrier)
+  constexpr bool A16 = F16 && !DUAL;
+  uint32_t* mult_tab = reinterpret_cast<uint32_t*>(smem + U * A_SLOT);
+  const int nb = p.exp_blocks;
+  auto mult_of = [&](int kt) __attribute__((always_inline)) {
+    return mult_tab[ar * nb + (kt0 + min(kt, nk - 1)) * KE / kHBlock];
+  };
+  if constexpr (A16) {
+    const int32_t* ex = p.a_exp + static_cast<long long>(job.row_begin + job.m0 +
+                                                         min(ar, job.rows_here - 1)) * nb;
+    int e_row = ex[0];
+    for (int b = 1; b < nb; ++b) e_row = max(e_row, ex[b]);
+    for (int b = ac; b < nb; b += 4)
+      mult_tab[ar * nb + b] = __builtin_bit_cast(uint32_t, pow2_neg_f16x2(e_row - ex[b]));
+    if (ac == 0) erow[ar] = e_row;
+    // the shifts of a row are read by the other lanes of this wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
   // weight tiles of this wave: lane l reads row l % 16 of the tile, bytes
   // [16 (l / 16), +16) of the slice.  Rows past N (a partial last tile, or
   // the router's N = E below 16) read row N - 1 instead: in bounds, and the
@@ -138,7 +192,16 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
       for (int t = 0; t < NT; ++t) dst[t] = gload<bf16x8>(b_src[t] + o);
     }
   };
-  auto store_a = [&](const uint4& v, int slot) __attribute__((always_inline)) {
+  // a slice of A into LDS slot `slot`; F16 projection: first multiplied by
+  // its block's fp16 pair mbits (exact while the result stays normal)
+  auto store_a = [&](uint4 v, int slot, uint32_t mbits) __attribute__((always_inline)) {
+    if constexpr (A16) {
+      const half2v mult = __builtin_bit_cast(half2v, mbits);
+      v.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, v.x) * mult);
+      v.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, v.y) * mult);
+      v.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, v.z) * mult);
+      v.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, v.w) * mult);
+    }
     *reinterpret_cast<uint4*>(smem + slot * A_SLOT + a_dst) = v;
   };
 
@@ -155,15 +218,16 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
     load_a(a_stage[j], j);
     load_b(b_ring[j - 1], j - 1);
   }
-  store_a(a_stage[0], 0);
+  store_a(a_stage[0], 0, A16 ? mult_of(0) : 0u);
 
   auto iter = [&](auto rc, int kt) __attribute__((always_inline)) {
     constexpr int R = decltype(rc)::value;  // kt % U
+    const uint32_t mb = A16 ? mult_of(kt + 1) : 0u;  // completes with the barrier's wait
     slice_barrier();                        // slice kt is in LDS for every wave
-    store_a(a_stage[(R + 1) % U], (R + 1) % U);
+    store_a(a_stage[(R + 1) % U], (R + 1) % U, mb);
     load_a(a_stage[R], kt + U);
     load_b(b_ring[(R + U - 1) % U], kt + U - 1);
-    if constexpr (MS > 0) {
+    if constexpr (MS > 0 && !A16) {
       const char* As = smem + R * A_SLOT;
       bf16x8 af[8];
 #pragma unroll
@@ -182,6 +246,38 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
       for (int i = 0; i < MS * NT; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         if (i % 4 == 3 && i / 4 < 1 + NT) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
+      }
+    }
+    if constexpr (MS > 0 && A16) {
+      // fp16 A fragments; weight tile t converted to fp16 just before its
+      // MS MFMAs (weight tile major, so each conversion overlaps the MFMAs
+      // of the tile before)
+      const char* As = smem + R * A_SLOT;
+      half8 af[8];
+#pragma unroll
+      for (int m = 0; m < MS; ++m)
+        af[m] = *reinterpret_cast<const half8*>(As + swz(m * 16 + (lane & 15), lane >> 4));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const half8 bf = bf16x8_to_f16(b_ring[R][t]);
+#pragma unroll
+        for (int m = 0; m < MS; ++m)
+          acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[m], bf, acc[m][t], 0, 0, 0);
+      }
+      // instruction order: fragment reads, the LDS write of the next slice,
+      // then per weight tile its conversion (12 VALU) and its MS MFMAs, the
+      // five global loads spread among them
+      __builtin_amdgcn_sched_group_barrier(0x100, MS, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          const int i = t * MS + m;
+          if (i % 4 == 3 && i / 4 < 1 + NT) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
+        }
       }
     }
   };
@@ -212,6 +308,42 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
           Cs[(m * 16 + lgrp * 4 + i) * LDC + wave * 32 + t * 16 + lrow] =
               silu_mul(acc[m][t][i], acc[m][t + 2][i]);
     __syncthreads();
+    if constexpr (F16) {
+      // per row: the 32 lanes of a half wave hold its 256 columns; the
+      // block's exponent e puts its largest |h| * 2^-e in [2^14, 2^15)
+      static_assert(BM * 32 % THREADS == 0, "every lane takes part in each row's reduction");
+      for (int q = tid; q < BM * 32; q += THREADS) {
+        const int r = q >> 5;
+        const int c8 = (q & 31) * 8;
+        const int n = job.n0 + c8;
+        const float* src = Cs + r * LDC + c8;
+        float v[8];
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          v[i] = src[i];
+          if (n + i < N) amax = fmaxf(amax, fabsf(v[i]));
+        }
+#pragma unroll
+        for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+        // amax = f * 2^x, f in [0.5, 1): e = x - 15; zeros (and inf/NaN) keep e = 0
+        const int e = (amax > 0.f && amax <= 3.402823466e38f) ? __builtin_amdgcn_frexp_expf(amax) - 15 : 0;
+        if (r >= job.rows_here || n >= N) continue;
+        const long long row = job.row_begin + job.m0 + r;
+        char* dst = gemm_out_row<2>(p, row);
+        if (c8 == 0) p.c_exp[row * p.exp_blocks + job.n0 / kHBlock] = e;
+        if (n + 8 <= N) {
+          half8 o;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[i] = static_cast<_Float16>(ldexpf(v[i], -e));
+          *reinterpret_cast<half8*>(dst + static_cast<long long>(n) * 2) = o;
+        } else {
+          for (int i = 0; n + i < N; ++i)
+            reinterpret_cast<_Float16*>(dst)[n + i] = static_cast<_Float16>(ldexpf(v[i], -e));
+        }
+      }
+      return;
+    }
     for (int q = tid; q < BM * 32; q += THREADS) {
       const int r = q >> 5;
       const int c8 = (q & 31) * 8;
@@ -254,13 +386,16 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
         if (r < job.rows_here && n < N) {
           const float* src = Cs + r * LDC + c4;
           float* dst = reinterpret_cast<float*>(gemm_out_row<4>(p, job.row_begin + job.m0 + r));
+          const int e = A16 ? erow[r] : 0;  // A16: the row's exponent
+          const f32x4 o = A16 ? f32x4{ldexpf(src[0], e), ldexpf(src[1], e), ldexpf(src[2], e),
+                                      ldexpf(src[3], e)}
+                              : f32x4{src[0], src[1], src[2], src[3]};
           if (n + 4 <= N) {
             // y is read once, by the combine: nontemporal stores keep it from
             // evicting the weight slices the other m-tiles still read from L2
-            __builtin_nontemporal_store(f32x4{src[0], src[1], src[2], src[3]},
-                                        reinterpret_cast<f32x4*>(dst + n));
+            __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(dst + n));
           } else {
-            for (int i = 0; n + i < N; ++i) dst[n + i] = src[i];
+            for (int i = 0; n + i < N; ++i) dst[n + i] = o[i];
           }
         }
       }
@@ -269,11 +404,14 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
   }
 }
 
-template <bool DUAL, bool PARTN>
+template <bool DUAL, bool PARTN, bool F16>
 __global__ __launch_bounds__(THREADS, 1) void gemm_prefill_kernel(GemmLaunch p) {
   constexpr int BN = DUAL ? 256 : 512;  // output columns per block
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
-  static_assert(U * A_SLOT <= SMEM, "A ring inside the epilogue tile");
+  __shared__ int erow[BM];
+  static_assert(U * A_SLOT + BM * kMaxHBlocks * 4 <= SMEM,
+                "A ring and block shifts inside the epilogue tile");
+  static_assert(!DUAL || BN == kHBlock, "one exponent per gate/up tile row");
 
   TileJob job;
   if (!find_tile<BM, BN, DUAL>(p, job)) return;
@@ -294,11 +432,11 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_prefill_kernel(GemmLaunch p) 
   const bool n_act = DUAL ? (!PARTN || job.n0 + wave * 32 < N) : job.n0 + wave * 64 < N;
   const int ms = n_act ? min(4, (job.rows_here + 31) >> 5) * 2 : 0;
   switch (ms) {
-    case 8: tile_body<DUAL, 8>(p, job, smem, nk, kt0); break;
-    case 6: tile_body<DUAL, 6>(p, job, smem, nk, kt0); break;
-    case 4: tile_body<DUAL, 4>(p, job, smem, nk, kt0); break;
-    case 2: tile_body<DUAL, 2>(p, job, smem, nk, kt0); break;
-    default: tile_body<DUAL, 0>(p, job, smem, nk, kt0); break;
+    case 8: tile_body<DUAL, 8, F16>(p, job, smem, nk, kt0, erow); break;
+    case 6: tile_body<DUAL, 6, F16>(p, job, smem, nk, kt0, erow); break;
+    case 4: tile_body<DUAL, 4, F16>(p, job, smem, nk, kt0, erow); break;
+    case 2: tile_body<DUAL, 2, F16>(p, job, smem, nk, kt0, erow); break;
+    default: tile_body<DUAL, 0, F16>(p, job, smem, nk, kt0, erow); break;
   }
 }
 
@@ -316,10 +454,24 @@ hipError_t launch_prefill(const GemmLaunch& g, hipStream_t st) {
   const long long grid = ((total + 7) / 8) * 8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 gd(static_cast<unsigned>(grid), static_cast<unsigned>(splits));
-  if (DUAL && g.N % BN != 0)
-    hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, true>), gd, dim3(THREADS), 0, st, g);
-  else
-    hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, false>), gd, dim3(THREADS), 0, st, g);
+  const bool f16 = DUAL ? g.c_exp != nullptr : g.a_exp != nullptr;
+  if (f16) {
+    // one exponent per 256 columns of h: gate/up tiles are 256 wide; the
+    // projection's shift table has room for kMaxHBlocks blocks per row
+    if (g.exp_blocks != ((DUAL ? g.N : g.K) + kHBlock - 1) / kHBlock || g.exp_blocks > kMaxHBlocks)
+      return hipErrorInvalidValue;
+    if (!DUAL && g.k_splits > 1) return hipErrorInvalidValue;
+  }
+  if (DUAL && g.N % BN != 0) {
+    if (f16)
+      hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, true, true>), gd, dim3(THREADS), 0, st, g);
+    else
+      hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, true, false>), gd, dim3(THREADS), 0, st, g);
+  } else if (f16) {
+    hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, false, true>), gd, dim3(THREADS), 0, st, g);
+  } else {
+    hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, false, false>), gd, dim3(THREADS), 0, st, g);
+  }
   return hipGetLastError();
 }
 

@@ -50,6 +50,8 @@ moe_status_t check_config(const moe_config_t* c) {
   // I = 256 8.7e-2 rms (over the 6e-2 fp8 bar), I = 512 4.3e-2, I >= 768
   // <= 3.4e-2.  Below 512 the library does not run fp8.
   if (c->expert_dtype == MOE_FP8_E4M3 && c->I < kFp8MinI) return MOE_ERR_UNSUPPORTED;
+  // bf16 h in scaled fp16 keeps one exponent per 256 columns in LDS
+  if (c->expert_dtype == MOE_BF16 && c->I > kHBlock * kMaxHBlocks) return MOE_ERR_UNSUPPORTED;
   // group-limited routing: n_group 0 or 1 means none
   if (c->n_group < 0) return MOE_ERR_INVALID_ARG;
   if (c->n_group > 1) {
@@ -204,6 +206,8 @@ GemmLaunch gate_up_launch(const moe_config_t& c, const Layout& L, const void* x,
   g.ldc = c.I;
   g.c_scale = fp8 ? at<float>(ws, L.hs) : nullptr;
   g.C_lo = L.h_split ? at<char>(ws, L.hlo) : nullptr;
+  g.c_exp = L.h_f16 ? at<int32_t>(ws, L.hexp) : nullptr;
+  g.exp_blocks = (c.I + kHBlock - 1) / kHBlock;
   g.w_tiled = c.expert_layout == MOE_LAYOUT_TILED;
   return g;
 }
@@ -319,6 +323,8 @@ GemmLaunch down_launch(const moe_config_t& c, const Layout& L, void* y_sorted, v
   g.c_split = static_cast<long long>(c.T) * c.k;
   g.ldc = c.H;
   g.A_lo = L.h_split ? at<char>(ws, L.hlo) : nullptr;
+  g.a_exp = L.h_f16 ? at<int32_t>(ws, L.hexp) : nullptr;
+  g.exp_blocks = (c.I + kHBlock - 1) / kHBlock;
   g.w_tiled = c.expert_layout == MOE_LAYOUT_TILED;
   return g;
 }
@@ -387,6 +393,11 @@ Layout make_layout(const moe_config_t& c) {
   // every h element, which shows in the layer output next to the output's own
   // bf16 rounding; the large-tile prefill kernel is MFMA-bound and keeps one.
   L.h_split = c.expert_dtype == MOE_BF16 && !(L.dn.bm == 128 && L.dn.bn == 512);
+  // The large-tile kernel is MFMA-bound, so a second product for h's residue
+  // is not free there.  It keeps h in fp16 instead (3 more significant bits
+  // than bf16, same MFMA rate), scaled by a power of two per row and block of
+  // 256 h columns so that the fp16 range holds any h.
+  L.h_f16 = c.expert_dtype == MOE_BF16 && !L.h_split;
   L.router = TileShape{64, T <= 2048 ? 128 : 64};
   // bf16 at small T: the weight-streaming kernel (gemm_decode.hip), 16 token
   // rows x 256 experts per block, K split as below
@@ -447,6 +458,7 @@ Layout make_layout(const moe_config_t& c) {
   L.xs = take(fp8 ? T * (H / kQBlock) * 4 : 0);
   L.h = take(rows_all * I * (fp8 ? 1 : asz));
   L.hlo = take(L.h_split ? rows_all * I * 2 : 0);
+  L.hexp = take(L.h_f16 ? rows_all * ((I + kHBlock - 1) / kHBlock) * 4 : 0);
   L.hs = take(fp8 ? rows_all * (I / kQBlock) * 4 : 0);
   L.y = take(R * H * 4);        // fp32: rounded once, in the combine
   L.ysh = take(S * T * H * 4);
@@ -496,6 +508,7 @@ size_t moe_workspace_offset(const moe_config_t* cfg, int32_t part) {
     case MOE_WS_H: return L.h;
     case MOE_WS_H_SCALES: return fp8 ? L.hs : kNone;
     case MOE_WS_H_LO: return L.h_split ? L.hlo : kNone;
+    case MOE_WS_H_EXP: return L.h_f16 ? L.hexp : kNone;
     case MOE_WS_Y: return L.y;
     case MOE_WS_Y_SHARED: return cfg->S > 0 ? L.ysh : kNone;
     default: return kNone;

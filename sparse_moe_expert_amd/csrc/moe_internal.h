@@ -21,6 +21,8 @@ constexpr int kQBlock = 128;          // FP8 scale granularity along K
 constexpr int kDispatchChunk = 1024;  // flat (token, slot) pairs per dispatch wave
 constexpr float kTieEps = 1e-6f;
 constexpr int kFp8MinI = 512;         // smallest intermediate size run in FP8
+constexpr int kHBlock = 256;          // h columns per exponent of the scaled fp16 h
+constexpr int kMaxHBlocks = 64;       // so I <= 16384 on the large-tile bf16 path
 
 // One GEMM group = one expert (routed e < E, shared E + s) over a contiguous
 // range of rows of the sorted row space.  Rows [0, R) are the routed (token,
@@ -62,6 +64,7 @@ struct Layout {
   size_t xs;            // FP8: [T, H/128] fp32 scales
   size_t h;             // [R + S*T, I] act type, or e4m3 codes (FP8)
   size_t hlo;           // bf16 h_split: [R + S*T, I] bf16 residue h - bf16(h)
+  size_t hexp;          // bf16 h_f16: [R + S*T, ceil(I / kHBlock)] int32 block exponents
   size_t hs;            // FP8: [R + S*T, I/128] fp32 scales
   size_t y;             // [R, H] fp32  (routed expert outputs, sorted)
   size_t ysh;           // [S, T, H] fp32
@@ -70,6 +73,7 @@ struct Layout {
   int nchunks;
   int router_splits;    // >= 1
   bool h_split;         // bf16 h kept as hi + lo (down GEMM on an HBM-bound kernel)
+  bool h_f16;           // bf16 experts on the large-tile kernel: h as scaled fp16
   TileShape gu, dn, router;
 };
 
@@ -132,6 +136,13 @@ struct GemmLaunch {
   // with the stride and row mapping of A
   void* C_lo;
   const void* A_lo;
+  // scaled fp16 h (large-tile kernel only; null = not used): the gate/up GEMM
+  // stores v * 2^-e in fp16, e per row and block of kHBlock h columns chosen
+  // so that the block's largest |v| * 2^-e lies in [2^14, 2^15), with e in
+  // c_exp [rows, exp_blocks]; the down GEMM reads A that way through a_exp
+  int32_t* c_exp;
+  const int32_t* a_exp;
+  int exp_blocks;
   // split K (generic kernel, fp32 output only): block y computes the K range
   // [y * K / k_splits, (y + 1) * K / k_splits) into C + y * c_split_stride
   int k_splits;            // 0 or 1: no split

@@ -98,6 +98,9 @@ def cfg(**kw):
     (dict(act="bf16", expert="fp8", I=640, tiled=True), True),
     (dict(act="bf16", expert="fp8", I=512, tiled=True), True),
     (dict(act="bf16", expert="fp8", H=640, I=512, tiled=True), True),
+    # bf16 experts: at most 16384 intermediate channels (64 blocks of scaled h)
+    (dict(act="bf16", expert="bf16", I=16384, T=4), True),
+    (dict(act="bf16", expert="bf16", I=16512, T=4), False),
 ])
 def test_workspace_size_validates(kw, ok):
     n = moe.moe_workspace_size(cfg(**kw))
@@ -108,10 +111,11 @@ def test_workspace_size_covers_buffers():
     c = moe.make_config(T=16384, H=5120, E=256, S=1, k=8, I=1536)
     n = moe.moe_workspace_size(c)
     R = 16384 * 8
-    # h (bf16) + y_sorted and y_shared (fp32) + router logits (fp32, K split
-    # 2 ways at this T) + the normalised block input (bf16)
-    need = ((R + 16384) * 1536 * 2 + R * 5120 * 4 + 16384 * 5120 * 4 + 2 * 16384 * 256 * 4
-            + 16384 * 5120 * 2)
+    # h (fp16 codes) and its block exponents (6 per row) + y_sorted and
+    # y_shared (fp32) + router logits (fp32, K split 2 ways at this T) + the
+    # normalised block input (bf16)
+    need = ((R + 16384) * 1536 * 2 + (R + 16384) * 6 * 4 + R * 5120 * 4 + 16384 * 5120 * 4
+            + 2 * 16384 * 256 * 4 + 16384 * 5120 * 2)
     assert need <= n < need * 1.05
 
 
@@ -247,7 +251,8 @@ def test_pack_validation():
 def test_workspace_offsets():
     """moe_workspace_offset: every part lies inside the workspace, in the order
     of the carve-out; h's bf16 residue exists only where the down GEMM streams
-    its weights (not on the T=16384 large-tile path, not for fp8 or fp32)."""
+    its weights, h's block exponents only on the bf16 large-tile path (T=16384),
+    neither for fp8."""
     parts = [moe.MOE_WS_TOPK_IDX, moe.MOE_WS_TOPK_W, moe.MOE_WS_COUNTS, moe.MOE_WS_OFFSETS,
              moe.MOE_WS_PERM, moe.MOE_WS_INV, moe.MOE_WS_H, moe.MOE_WS_H_LO, moe.MOE_WS_Y,
              moe.MOE_WS_Y_SHARED]
@@ -262,12 +267,17 @@ def test_workspace_offsets():
     big = moe.make_config(T=16384, H=5120, E=256, S=1, k=8, I=1536)
     assert moe.moe_workspace_offset(big, moe.MOE_WS_H_LO) is None
     assert moe.moe_workspace_offset(big, moe.MOE_WS_H) is not None
+    assert moe.moe_workspace_offset(dec, moe.MOE_WS_H_EXP) is None
+    hb, ex = (moe.moe_workspace_offset(big, p) for p in (moe.MOE_WS_H, moe.MOE_WS_H_EXP))
+    assert ex is not None and ex - hb >= (16384 * 9) * 1536 * 2
+    assert ex + (16384 * 9) * 6 * 4 <= moe.moe_workspace_size(big)
     f8 = moe.make_config(T=256, H=5120, E=256, S=1, k=8, I=1536, expert="fp8")
     assert moe.moe_workspace_offset(f8, moe.MOE_WS_H_LO) is None
+    assert moe.moe_workspace_offset(f8, moe.MOE_WS_H_EXP) is None
     assert moe.moe_workspace_offset(f8, moe.MOE_WS_H_SCALES) is not None
     s0 = moe.make_config(T=64, H=512, E=8, S=0, k=2, I=128)
     assert moe.moe_workspace_offset(s0, moe.MOE_WS_Y_SHARED) is None
-    assert moe.moe_workspace_offset(dec, 11) is None and moe.moe_workspace_offset(dec, -1) is None
+    assert moe.moe_workspace_offset(dec, 12) is None and moe.moe_workspace_offset(dec, -1) is None
     assert moe.moe_workspace_offset(moe.make_config(T=1, H=100, E=8, S=1, k=2, I=128),
                                     moe.MOE_WS_H) is None
 

@@ -279,18 +279,7 @@ LAYER_CASES = {
 
 
 # Cases that miss the bar, with the measured reason (kept, expected to fail).
-LAYER_XFAIL = {
-    # One expert, k = 1, no shared expert: out is one expert's y, with no
-    # other term beside it.  The largest |out| is 5.9 rms, and rounding the
-    # exact output to bf16 alone costs 1.39e-2 rms there; the MFMA-bound
-    # large-tile kernel rounds h to bf16 once, which adds ~0.6e-2 at that
-    # element (measured 2.01e-2 against the 2e-2 bar).
-    "bf16_T4096_E1_dense": "one bf16 rounding of h in the large-tile kernel: 2.01e-2 rms",
-    # the same cause; output rounding alone 1.63e-2 (|out| up to 7.9 rms) and
-    # 1.76e-2 rms, with one bf16 rounding of h 2.70e-2 and 2.25e-2 rms
-    "bf16_T4096_E8": "one bf16 rounding of h in the large-tile kernel: 2.70e-2 rms",
-    "bf16_T4096_E100": "one bf16 rounding of h in the large-tile kernel: 2.25e-2 rms",
-}
+LAYER_XFAIL = {}
 
 
 @pytest.mark.parametrize("case", [
@@ -319,7 +308,7 @@ def test_layer_forward_small(case):
 INTERMEDIATE_CASES = {
     "bf16_decode_split": lambda: small(T=64, H=512, E=64, S=1, k=4, I=256),
     "bf16_mid_split": lambda: small(T=256, H=768, E=32, S=1, k=8, I=256),
-    "bf16_big_one_term": lambda: small(T=600, H=512, E=32, S=2, k=8, I=384),
+    "bf16_big_scaled_f16": lambda: small(T=600, H=512, E=32, S=2, k=8, I=384),
     "fp8_small": lambda: small(T=200, H=512, E=16, S=1, k=4, I=1536, expert="fp8"),
     "fp8_decode": lambda: small(T=64, H=512, E=16, S=2, k=4, I=1536, expert="fp8"),
     "fp8_midT": lambda: small(T=700, H=512, E=16, S=2, k=4, I=1536, expert="fp8"),
@@ -329,9 +318,11 @@ INTERMEDIATE_CASES = {
 @pytest.mark.parametrize("case", list(INTERMEDIATE_CASES))
 def test_layer_intermediates(case):
     """h and y as the layer leaves them in its workspace.
-    bf16: h (plus its bf16 residue where the layout keeps one) within its
-    rounding of the exact h: 2^-8 relative for one bf16 term, 2^-16 for two,
-    plus 1e-5 rms(h) of fp32 accumulation.
+    bf16: h within its rounding of the exact h plus 1e-5 rms(h) of fp32
+    accumulation: 2^-16 relative for two bf16 terms (h and its residue); for
+    scaled fp16 codes c with block exponents e (h = c * 2^e), 2^-11 relative
+    plus 2^-25 * 2^e (fp16 subnormals), and each block's largest |c| in
+    [2^14, 2^15] (or a block of zeros with e = 0).
     fp8: h codes equal the oracle's except at rounding boundaries (see
     check_fp8_h_codes); then y, recomputed by the oracle from the GPU's own h
     codes, within 1e-3 rms (the fp8 MFMA's ~17-bit group sums); and the layer
@@ -357,16 +348,29 @@ def test_layer_intermediates(case):
                .cpu().numpy() if cfg.S else np.zeros((0, cfg.T, cfg.H)))
     W = oracle.Weights(cfg, inp)
     if cfg.expert == "bf16":
-        hi = oracle.decode_bf16(ws_part(moe, c, ws, moe.MOE_WS_H, torch.int16, (rows_all, cfg.I))
-                                .cpu().numpy().view(np.uint16))
-        lo_off = moe.moe_workspace_offset(c, moe.MOE_WS_H_LO)
-        split = lo_off is not None
-        h_gpu = hi + (oracle.decode_bf16(ws_part(moe, c, ws, moe.MOE_WS_H_LO, torch.int16,
-                                                 (rows_all, cfg.I)).cpu().numpy().view(np.uint16))
-                      if split else 0.0)
-        rel = 2.0 ** -16 if split else 2.0 ** -8
-        excess = np.abs(h_gpu - h_ref) - rel * np.abs(h_ref)
-        log(f"intermediates {case}: h {'two' if split else 'one'} bf16 term(s); max (|Δh| - "
+        split = moe.moe_workspace_offset(c, moe.MOE_WS_H_LO) is not None
+        scaled = moe.moe_workspace_offset(c, moe.MOE_WS_H_EXP) is not None
+        assert split != scaled, "bf16 h is either two bf16 terms or scaled fp16"
+        if split:
+            h_gpu = (oracle.decode_bf16(ws_part(moe, c, ws, moe.MOE_WS_H, torch.int16,
+                                                (rows_all, cfg.I)).cpu().numpy().view(np.uint16))
+                     + oracle.decode_bf16(ws_part(moe, c, ws, moe.MOE_WS_H_LO, torch.int16,
+                                                  (rows_all, cfg.I)).cpu().numpy().view(np.uint16)))
+            bound = 2.0 ** -16 * np.abs(h_ref)
+        else:
+            nb = -(-cfg.I // 256)
+            codes = (ws_part(moe, c, ws, moe.MOE_WS_H, torch.float16, (rows_all, cfg.I))
+                     .cpu().numpy().astype(np.float64))
+            ex = ws_part(moe, c, ws, moe.MOE_WS_H_EXP, torch.int32, (rows_all, nb)).cpu().numpy()
+            ex_col = np.repeat(ex, 256, axis=1)[:, :cfg.I].astype(np.float64)
+            h_gpu = codes * np.exp2(ex_col)
+            bound = 2.0 ** -11 * np.abs(h_ref) + 2.0 ** -25 * np.exp2(ex_col)
+            for b in range(nb):
+                amax = np.abs(codes[:, 256 * b:256 * (b + 1)]).max(axis=1)
+                ok = ((amax >= 2.0 ** 14) & (amax <= 2.0 ** 15)) | ((amax == 0) & (ex[:, b] == 0))
+                assert ok.all(), f"{case}: block {b} codes out of [2^14, 2^15]: {amax[~ok][:4]}"
+        excess = np.abs(h_gpu - h_ref) - bound
+        log(f"intermediates {case}: h {'two bf16 terms' if split else 'scaled fp16'}; max (|Δh| - "
             f"rounding)/rms(h) = {max(excess.max(), 0) / oracle.rms(h_ref):.3e}")
         assert excess.max() <= 1e-5 * oracle.rms(h_ref)
         return
