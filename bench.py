@@ -54,7 +54,7 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE layer fwd tokens/s & TFLOP/s (T=16384); HBM GB/s at T=256; % roofline"
 GEMM_SRCS = [os.path.join(ROOT, "sparse_moe_expert_amd", "csrc", f)
-             for f in ("gemm.hip", "gemm_prefill.hip", "gemm_big.hip", "gemm_decode.hip",
+             for f in ("gemm.hip", "gemm_prefill.hip", "gemm_big.hip", "gemm_fp8.hip", "gemm_decode.hip",
                        "gemm_decode_device.h", "gemm_sched.h", "moe_device.h", "moe_internal.h")]
 EXPERT_KEYS = ("w_gate_up", "w_down", "w_sh_gate_up", "w_sh_down")
 

@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["moe_api.hip", "gemm.hip", "gemm_prefill.hip", "gemm_big.hip", "gemm_decode.hip", "route.hip", "dispatch.hip",
+SOURCES = ["moe_api.hip", "gemm.hip", "gemm_prefill.hip", "gemm_big.hip", "gemm_fp8.hip", "gemm_decode.hip", "route.hip", "dispatch.hip",
            "combine.hip", "norm.hip", "fused.hip", "pack.hip", "probe.hip"]
 
 HIPCC_FLAGS = [

@@ -490,6 +490,10 @@ hipError_t launch_gemm(int a_kind, int out_kind, TileShape ts, const GemmLaunch&
     return launch_gemm_prefill(dual, g, st);
   }
   if (g.c_exp || g.a_exp) return hipErrorInvalidValue;  // scaled fp16 h: large-tile kernel only
+  if (gemm_fp8s_supported(a_kind, out_kind, ts, dual)) {
+    if (g.A_lo || g.C_lo) return hipErrorInvalidValue;
+    return launch_gemm_fp8s(dual, g, st);
+  }
   if (gemm_big_supported(a_kind, out_kind, ts, dual)) {
     if (g.A_lo || g.C_lo) return hipErrorInvalidValue;  // one-term h only
     return launch_gemm_big(a_kind, out_kind, dual, g, st);

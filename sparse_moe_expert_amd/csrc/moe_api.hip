@@ -383,6 +383,11 @@ Layout make_layout(const moe_config_t& c) {
       L.gu = TileShape{128, 256};
       L.dn = TileShape{128, 512};
     }
+  } else if (fp8 && bm == 128 && avg <= 192.0 && H <= 8192 && I <= 8192) {
+    // up to 192 rows per expert: one 192-row tile streams each expert's
+    // weights once (gemm_fp8.hip)
+    L.gu = TileShape{192, 128};
+    L.dn = TileShape{192, 256};
   } else if (fp8 && bm == 128) {
     L.gu = TileShape{128, 256};
     L.dn = TileShape{128, 512};

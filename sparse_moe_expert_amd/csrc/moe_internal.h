@@ -159,6 +159,10 @@ hipError_t launch_gemm(int a_kind, int out_kind, TileShape ts, const GemmLaunch&
 bool gemm_prefill_supported(int a_kind, int out_kind, TileShape ts, bool dual);
 hipError_t launch_gemm_prefill(bool dual, const GemmLaunch& g, hipStream_t st);
 // Large-tile fp8 kernel (gemm_big.hip), same tile shapes.
+// Weight-streaming FP8 kernel (gemm_fp8.hip): 192 token rows x 128 h-columns
+// (gate/up) or 192 rows x 256 output columns (projection), e4m3 operands.
+bool gemm_fp8s_supported(int a_kind, int out_kind, TileShape ts, bool dual);
+hipError_t launch_gemm_fp8s(bool dual, const GemmLaunch& g, hipStream_t st);
 bool gemm_big_supported(int a_kind, int out_kind, TileShape ts, bool dual);
 hipError_t launch_gemm_big(int a_kind, int out_kind, bool dual, const GemmLaunch& g,
                            hipStream_t st);
