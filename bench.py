@@ -244,7 +244,7 @@ def rows_stats(counts):
 
 # ---------------------------------------------------------------- sub-lines
 
-def decode_line(cfg, steps, extras):
+def decode_line(cfg, steps, extras, fused=True):
     """T=256 tokens on the decode-sized workload's own seeded weights: the
     weight-streaming regime, measured against 8 TB/s."""
     import sparse_moe_expert_amd as moe
@@ -253,10 +253,11 @@ def decode_line(cfg, steps, extras):
     r = time_layer(lay, steps, 5)
     b = layer_bytes(cfg, r["counts"])
     gbs = b / (r["ms"] / 1e3) / 1e9
-    out1 = lay.empty_out()
-    msf = time_calls(lambda: moe.moe_layer_forward_fused(
-        lay.ccfg, lay.weights, lay.t["x"], out1, None, None, lay.workspace), steps, 5)
-    gbf = b / (msf / 1e3) / 1e9
+    if fused:
+        out1 = lay.empty_out()
+        msf = time_calls(lambda: moe.moe_layer_forward_fused(
+            lay.ccfg, lay.weights, lay.t["x"], out1, None, None, lay.workspace), steps, 5)
+        gbf = b / (msf / 1e3) / 1e9
     res = {
         "workload": cfg.name, "ms_per_step": round(r["ms"], 4),
         "ms_per_step_instrumented": round(r["ms_inst"], 4),
@@ -267,9 +268,10 @@ def decode_line(cfg, steps, extras):
         "tflops": round(cfg.flops() / (r["ms"] / 1e3) / 1e12, 2),
         "stages_ms": stage_dict(r), "experts_touched": int((r["counts"] > 0).sum()),
         "near_tie_tokens": {"selection": r["ties"][0], "slot_order": r["ties"][1]},
-        "fused_single_launch": {"ms_per_step": round(msf, 4), "hbm_GBps": round(gbf, 1),
-                                "frac_of_hbm_peak": round(gbf / PEAK_HBM_GBS, 4)},
     }
+    if fused:
+        res["fused_single_launch"] = {"ms_per_step": round(msf, 4), "hbm_GBps": round(gbf, 1),
+                                      "frac_of_hbm_peak": round(gbf / PEAK_HBM_GBS, 4)}
     if rows is not None:
         msr = time_layer(rows, steps, 5)["ms"]
         g1r = b / (msr / 1e3) / 1e9
@@ -455,6 +457,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the T=256 line")
     ap.add_argument("--no-workloads", action="store_true", help="skip the T=8192 and fp8 lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the single-launch (cooperative) layer in the T=256 line")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--no-extras", action="store_true",
                     help="skip ceilings, grouped routing, block, copy and row-major lines")
@@ -532,7 +536,8 @@ def main():
         gc.collect()
         torch.cuda.empty_cache()
         if not args.no_decode:
-            res["decode_T256"], l1 = decode_line(config(1), args.decode_steps, extras)
+            res["decode_T256"], l1 = decode_line(config(1), args.decode_steps, extras,
+                                                 fused=not args.no_fused)
             del l1
             gc.collect()
             torch.cuda.empty_cache()
