@@ -194,6 +194,11 @@ size_t moe_workspace_size(const moe_config_t* cfg);
  *                                      of zeros)
  *  MOE_WS_Y          fp32  [T*k, H]    routed expert outputs, sorted rows
  *  MOE_WS_Y_SHARED   fp32  [S, T, H]   shared expert outputs
+ *  MOE_WS_BARRIER    uint32 [2]        moe_layer_forward_fused only: its grid
+ *                                      barrier's arrival count, then a status
+ *                                      word, 0 after a completed launch and
+ *                                      1 if a barrier wait timed out (the
+ *                                      outputs are then incomplete)
  * Returns the byte offset of `part` inside the workspace of
  * moe_layer_forward (and of the entry points that share it) for this config,
  * or (size_t)-1 if the config is invalid, `part` unknown, or the config holds
@@ -202,7 +207,7 @@ size_t moe_workspace_size(const moe_config_t* cfg);
 typedef enum {
   MOE_WS_TOPK_IDX = 0, MOE_WS_TOPK_W = 1, MOE_WS_COUNTS = 2, MOE_WS_OFFSETS = 3,
   MOE_WS_PERM = 4, MOE_WS_INV = 5, MOE_WS_H = 6, MOE_WS_H_SCALES = 7, MOE_WS_H_LO = 8,
-  MOE_WS_Y = 9, MOE_WS_Y_SHARED = 10, MOE_WS_H_EXP = 11
+  MOE_WS_Y = 9, MOE_WS_Y_SHARED = 10, MOE_WS_H_EXP = 11, MOE_WS_BARRIER = 12
 } moe_ws_part_t;
 size_t moe_workspace_offset(const moe_config_t* cfg, int32_t part);
 
@@ -313,11 +318,23 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
  * weights: bf16 activations and experts, at most 12 routed rows per expert
  * on average (T*k/E), E a multiple of 16; otherwise MOE_ERR_UNSUPPORTED and
  * nothing is enqueued.  The device must hold the whole grid at once
- * (checked by the cooperative launch; MOE_ERR_HIP if it cannot). */
+ * (checked by the cooperative launch; MOE_ERR_HIP if it cannot).  The grid
+ * barriers wait a bounded time (moe_fused_set_spin_limit): a launch whose
+ * wait runs out stops every block and leaves status 1 in the workspace's
+ * MOE_WS_BARRIER word 1, which the caller reads after synchronising the
+ * stream (the library never synchronises).  Calls that overlap on one
+ * workspace race on that counter. */
 moe_status_t moe_layer_forward_fused(const moe_config_t* cfg, const moe_weights_t* w,
                                      const void* x, void* out, int32_t* opt_counts,
                                      int32_t* opt_tie_counts, void* workspace,
                                      size_t workspace_bytes, moe_stream_t stream);
+
+/* Bound of each grid-barrier wait of moe_layer_forward_fused, in polls of
+ * the arrival counter (each an atomic load and a short sleep, about a
+ * microsecond); 0 gives up at the first poll that finds blocks missing (for
+ * tests of that path); polls < 0 restores the default (2^22).  Process-wide,
+ * read when a launch is enqueued.  Returns the previous value. */
+int64_t moe_fused_set_spin_limit(int64_t polls);
 
 /* RMSNorm of the decoder block [DD §3.3 figure "Residual + RMSNorm"; D1:
  * variance in fp32, rsqrt, times the weight]: for every row t of h [T, H]

@@ -19,7 +19,8 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 # moe_ws_part_t
 (MOE_WS_TOPK_IDX, MOE_WS_TOPK_W, MOE_WS_COUNTS, MOE_WS_OFFSETS, MOE_WS_PERM, MOE_WS_INV,
- MOE_WS_H, MOE_WS_H_SCALES, MOE_WS_H_LO, MOE_WS_Y, MOE_WS_Y_SHARED, MOE_WS_H_EXP) = range(12)
+ MOE_WS_H, MOE_WS_H_SCALES, MOE_WS_H_LO, MOE_WS_Y, MOE_WS_Y_SHARED, MOE_WS_H_EXP,
+ MOE_WS_BARRIER) = range(13)
 WS_NONE = (1 << 64) - 1
 
 # every entry point of include/moe.h
@@ -28,7 +29,8 @@ EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_version", "moe_wor
            "moe_dispatch", "moe_grouped_ffn", "moe_expert_gate_up", "moe_expert_down",
            "moe_combine", "moe_quantize_fp8", "moe_layer_forward", "moe_layer_forward_timed",
            "moe_rmsnorm", "moe_block_forward", "moe_layer_forward_fused",
-           "moe_pack_expert_weights", "moe_layer_forward_noalloc", "moe_stream_read")
+           "moe_pack_expert_weights", "moe_layer_forward_noalloc", "moe_stream_read",
+           "moe_fused_set_spin_limit")
 
 
 class MoEError(RuntimeError):
@@ -88,6 +90,7 @@ def _load():
         "moe_layer_forward_fused": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P, SZ, P]),
         "moe_layer_forward_noalloc": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P]),
         "moe_stream_read": (ctypes.c_int, [P, SZ, P, ctypes.c_int32, P]),
+        "moe_fused_set_spin_limit": (ctypes.c_int64, [ctypes.c_int64]),
         "moe_rmsnorm": (ctypes.c_int, [CP, P, P, ctypes.c_float, P, P]),
         "moe_block_forward": (ctypes.c_int, [CP, WP, P, P, ctypes.c_float, P, I32P, I32P, P, SZ,
                                              P]),
@@ -254,6 +257,12 @@ def moe_layer_forward_noalloc(cfg, weights, x, out, opt_counts=None, opt_tie_cou
 
 
 NOALLOC_SCRATCH_BYTES = 96 << 20
+
+
+def moe_fused_set_spin_limit(polls):
+    """Bound of each grid-barrier wait of moe_layer_forward_fused (0: give up
+    at once; polls < 0: the default); returns the previous bound."""
+    return int(LIB.moe_fused_set_spin_limit(int(polls)))
 
 
 def moe_stream_read(src, nbytes, sink, blocks, stream=None):

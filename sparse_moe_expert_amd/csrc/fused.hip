@@ -9,8 +9,11 @@
 //   A  router logits: 16 tokens x 16 experts x one K-split per wave, straight
 //      from global memory into v_mfma_f32_16x16x32_bf16 (fp32 partial sums)
 //   B  top-k per token (one wave each; adds the K-split partial sums in order)
-//   C  block 0 alone: histogram, exclusive scan, stable scatter (one wave, 64
-//      pairs per step in flat order, ballot peers) and the GEMM tile table
+//   C  dispatch: every block builds the expert histogram and its exclusive
+//      scan in LDS from all T*k choices (a few thousand integers), counts the
+//      pairs before its own slice of the flat order, and scatters that slice
+//      stably (64 pairs per step, ballot peers); the GEMM tile table is
+//      spread over the first blocks
 //   D  gate/up + SwiGLU tiles of the weight-streaming GEMM
 //   E  down tiles of the same GEMM
 //   F  combine, one token per block at a time
@@ -19,14 +22,12 @@
 // same integers.  Where the layer has few tokens, the launches and the
 // barriers between dependent kernels are what this removes.
 //
-// Measured at T=256 (dots3 decode shape): 2.50 ms against 2.29 ms for the
-// separate launches.  The grid barriers cost tens of microseconds each, the
-// phases other than the two GEMMs take 0.59 ms here against 0.09 ms as
-// separate kernels (block 0 works through the dispatch phase while the rest
-// of the grid spins), and the GEMM phases run at 2 waves per SIMD instead of
-// 3 (the kernel's register count is the largest of its phases).
-#include <hip/hip_cooperative_groups.h>
-
+// The grid barrier is the library's own: an arrival counter in the
+// workspace, polled with s_sleep by one thread per block, and a bounded wait.
+// A block that waits more than the spin limit (moe_fused_set_spin_limit)
+// sets the status word next to the counter; every block that sees it stops,
+// so the launch always ends, and the caller reads the status after
+// synchronising (MOE_WS_BARRIER).
 #include <algorithm>
 
 #include "combine_device.h"
@@ -36,12 +37,11 @@
 namespace moe {
 namespace {
 
-namespace cg = cooperative_groups;
 constexpr int kThreads = 256;  // 4 waves, the decode GEMM's tile
 constexpr int kGroupsMax = kMaxExperts + kMaxShared;
 
 // In-place exclusive scan of a[0, n) in LDS by one wavefront; returns the total.
-__device__ int wave_exclusive_scan(int* a, int n, int lane) {
+__device__ __forceinline__ int wave_exclusive_scan(int* a, int n, int lane) {
   const int seg = (n + 63) / 64;
   const int lo = min(n, lane * seg), hi = min(n, lo + seg);
   int sum = 0;
@@ -61,8 +61,44 @@ __device__ int wave_exclusive_scan(int* a, int n, int lane) {
   return __shfl(incl, 63, 64);
 }
 
+// Grid barrier number n (0, 1, ...), which every block meets once: thread 0
+// publishes the block's writes of the phase (release), adds its arrival and
+// polls until all gridDim.x blocks of this barrier have arrived (acquire).
+// Returns false in every thread of the block when the launch must stop: this
+// block polled more than spin_limit times (it then sets the status word) or
+// another block did.
+__device__ __forceinline__ bool grid_barrier(uint32_t* bar, long long spin_limit, unsigned n,
+                                             int* s_ok) {
+  __syncthreads();  // the block's writes of the phase are done
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    __threadfence();
+    __hip_atomic_fetch_add(&bar[0], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned target = (n + 1) * gridDim.x;
+    long long polls = 0;
+    // relaxed polls (an acquire per poll would invalidate the caches each
+    // time, under the blocks still working); one acquire fence after
+    while (__hip_atomic_load(&bar[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (__hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
+          ++polls > spin_limit) {
+        __hip_atomic_store(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+    if (__hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) ok = 0;
+    __atomic_thread_fence(__ATOMIC_ACQUIRE);
+    __threadfence();
+    *s_ok = ok;
+  }
+  __syncthreads();
+  return *s_ok != 0;
+}
+
 __global__ __launch_bounds__(kThreads, 2) void fused_decode_kernel(FusedArgs a) {
-  cg::grid_group grid = cg::this_grid();
+  __shared__ int s_ok;
+  unsigned nbar = 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -104,7 +140,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_decode_kernel(FusedArgs a) 
       }
     }
   }
-  grid.sync();
+  if (!grid_barrier(a.bar, a.spin_limit, nbar++, &s_ok)) return;
 
   // ---------------------------------------------------------------- B
   {
@@ -126,35 +162,49 @@ __global__ __launch_bounds__(kThreads, 2) void fused_decode_kernel(FusedArgs a) 
                              a.norm, a.rsf, a.idx, a.tw, a.ties, ti, lane, cbuf[wave]);
     }
   }
-  grid.sync();
+  if (!grid_barrier(a.bar, a.spin_limit, nbar++, &s_ok)) return;
 
   // ---------------------------------------------------------------- C
-  if (blockIdx.x == 0) {
+  {
     __shared__ int s_cnt[kMaxExperts], s_off[kMaxExperts], s_run[kMaxExperts];
     __shared__ int s_tg[kGroupsMax], s_td[kGroupsMax];
     const int R = a.T * a.k, E = a.E, G = a.E + a.S;
-    for (int e = tid; e < E; e += kThreads) s_cnt[e] = 0;
+    // this block's slice [f0, f1) of the flat (token, slot) order
+    const int sl = ((R + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x) + 63) / 64 * 64;
+    const int f0 = min(R, static_cast<int>(blockIdx.x) * sl), f1 = min(R, f0 + sl);
+    for (int e = tid; e < E; e += kThreads) {
+      s_cnt[e] = 0;
+      s_run[e] = 0;
+    }
     __syncthreads();
-    for (int f = tid; f < R; f += kThreads) atomicAdd(&s_cnt[a.idx[f]], 1);
+    // histogram of all pairs, and of the pairs before the slice
+    for (int f = tid; f < R; f += kThreads) {
+      const int e = a.idx[f];
+      atomicAdd(&s_cnt[e], 1);
+      if (f < f0) atomicAdd(&s_run[e], 1);
+    }
     __syncthreads();
     for (int e = tid; e < E; e += kThreads) s_off[e] = s_cnt[e];
     __syncthreads();
     if (wave == 0) wave_exclusive_scan(s_off, E, lane);
     __syncthreads();
     for (int e = tid; e < E; e += kThreads) {
-      a.counts[e] = s_cnt[e];
-      a.offsets[e] = s_off[e];
-      s_run[e] = s_off[e];
+      s_run[e] += s_off[e];  // first position of the slice's pairs of expert e
+      if (blockIdx.x == 0) {
+        a.counts[e] = s_cnt[e];
+        a.offsets[e] = s_off[e];
+      }
     }
-    if (tid == 0) a.offsets[E] = R;
+    if (blockIdx.x == 0 && tid == 0) a.offsets[E] = R;
     __syncthreads();
     if (wave == 0) {
-      // stable counting sort: 64 pairs per step in flat order; lanes with the
-      // same expert find each other with 9 ballots (one per bit of the id)
+      // stable counting sort of the slice: 64 pairs per step in flat order;
+      // lanes with the same expert find each other with 9 ballots (one per
+      // bit of the id)
       const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-      for (int f0 = 0; f0 < R; f0 += 64) {
-        const int f = f0 + lane;
-        const bool valid = f < R;
+      for (int fs = f0; fs < f1; fs += 64) {
+        const int f = fs + lane;
+        const bool valid = f < f1;
         const int e = valid ? a.idx[f] : 0;
         uint64_t peers = __ballot(valid);
 #pragma unroll
@@ -173,25 +223,28 @@ __global__ __launch_bounds__(kThreads, 2) void fused_decode_kernel(FusedArgs a) 
         }
       }
     }
-    // tile table of the two GEMMs: groups = routed experts, then shared
+    // tile table of the two GEMMs (groups = routed experts, then shared):
+    // every block scans the groups' tile counts, the first blocks write the
+    // descriptors and the m-tile -> group tables
     for (int gi = tid; gi < G; gi += kThreads) {
       const int rows = gi < E ? s_cnt[gi] : a.T;
       s_tg[gi] = (rows + a.tgu.bm - 1) / a.tgu.bm;
       s_td[gi] = (rows + a.tdn.bm - 1) / a.tdn.bm;
     }
     __syncthreads();
-    int tot_g = 0, tot_d = 0;
     if (wave == 0) {
-      tot_g = wave_exclusive_scan(s_tg, G, lane);
-      tot_d = wave_exclusive_scan(s_td, G, lane);
-      if (lane == 0) {
+      const int tot_g = wave_exclusive_scan(s_tg, G, lane);
+      const int tot_d = wave_exclusive_scan(s_td, G, lane);
+      if (blockIdx.x == 0 && lane == 0) {
         a.totals[0] = tot_g;
         a.totals[1] = tot_d;
       }
     }
     __syncthreads();
     const long long gu_elems = 2ll * a.I * a.H, dn_elems = static_cast<long long>(a.H) * a.I;
-    for (int gi = tid; gi < G; gi += kThreads) {
+    for (long long gl = static_cast<long long>(blockIdx.x) * kThreads + tid; gl < G;
+         gl += static_cast<long long>(gridDim.x) * kThreads) {
+      const int gi = static_cast<int>(gl);
       const bool shared = gi >= E;
       const long long e = shared ? gi - E : gi;
       GroupDesc d;
@@ -208,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_decode_kernel(FusedArgs a) 
       for (int i = 0; i < (d.rows + a.tdn.bm - 1) / a.tdn.bm; ++i) a.mtg_dn[d.tile_begin_dn + i] = gi;
     }
   }
-  grid.sync();
+  if (!grid_barrier(a.bar, a.spin_limit, nbar++, &s_ok)) return;
 
   // ---------------------------------------------------------------- D, E
   // tiles strided over the grid (a multiple of 8: tile b stays on XCD b % 8)
@@ -218,7 +271,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_decode_kernel(FusedArgs a) 
     for (long long vb = blockIdx.x; vb < ngu; vb += gridDim.x)
       decode_tile<1, true, 4>(a.gu, static_cast<int>(vb));
   }
-  grid.sync();
+  if (!grid_barrier(a.bar, a.spin_limit, nbar++, &s_ok)) return;
   {
     const long long ndn = ((static_cast<long long>(a.dn.grid_mtiles_upper) *
                                 ((a.dn.N + 255) / 256) + 7) / 8) * 8;
@@ -231,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_decode_kernel(FusedArgs a) 
         decode_tile<1, false, 4>(a.dn, static_cast<int>(vb));
     }
   }
-  grid.sync();
+  if (!grid_barrier(a.bar, a.spin_limit, nbar++, &s_ok)) return;
 
   // ---------------------------------------------------------------- F
   {
@@ -255,18 +308,23 @@ bool fused_decode_supported(TileShape gu, TileShape dn) {
 
 hipError_t launch_fused_decode(const FusedArgs& a, hipStream_t st) {
   if (a.T <= 0) return hipSuccess;
+  if (!a.bar || a.spin_limit < 0) return hipErrorInvalidValue;
   int dev = 0, cus = 0, per = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_decode_kernel, kThreads, 0);
   if (e != hipSuccess) return e;
-  // Every block must be resident at once (grid barriers), and no more than
-  // two per CU: the blocks that wait at a grid barrier spin, and with eight
-  // per CU a probe of this kernel's single-block dispatch phase stalled.  A
+  // Every block must be resident at once (grid barriers).  The kernel's 248
+  // VGPRs allow 2 waves per SIMD, so `per` is 2 (4-wave blocks); the cap
+  // keeps it there whatever a future build's register count allows.  A
   // multiple of 8 keeps the tile -> XCD mapping of the GEMM phases.
   const int grid = (std::min(per, 2) * cus) / 8 * 8;
   if (grid < 8) return hipErrorInvalidConfiguration;
+  // barrier counter and status word start at zero (a kernel, not a memset:
+  // the launch may be captured into a graph)
+  e = launch_zero_i32(reinterpret_cast<int32_t*>(a.bar), 2, st);
+  if (e != hipSuccess) return e;
   FusedArgs args = a;
   void* params[] = {&args};
   return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fused_decode_kernel), dim3(grid),

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <atomic>
 #include <mutex>
 
 #include "moe_internal.h"
@@ -337,6 +338,13 @@ hipError_t run_down(const moe_config_t& c, const Layout& L, void* y_sorted, void
 // Device address of `scratch` on the current device, looked up once per
 // device with that device current and kept for the process.
 constexpr int kMaxDevices = 64;
+// Polls of the single-launch layer's grid barrier before a block gives up
+// (moe_fused_set_spin_limit).  Each poll is an atomic load and a short sleep,
+// about a microsecond: the default bounds a wait at a few seconds, far above
+// the tens of microseconds a barrier takes.
+constexpr long long kDefaultFusedSpinLimit = 1ll << 22;
+std::atomic<long long> g_fused_spin_limit{kDefaultFusedSpinLimit};
+
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 
@@ -468,6 +476,7 @@ Layout make_layout(const moe_config_t& c) {
   L.y = take(R * H * 4);        // fp32: rounded once, in the combine
   L.ysh = take(S * T * H * 4);
   L.xn = take(T * H * asz);
+  L.fbar = take(8);
   L.total = off;
   return L;
 }
@@ -516,6 +525,7 @@ size_t moe_workspace_offset(const moe_config_t* cfg, int32_t part) {
     case MOE_WS_H_EXP: return L.h_f16 ? L.hexp : kNone;
     case MOE_WS_Y: return L.y;
     case MOE_WS_Y_SHARED: return cfg->S > 0 ? L.ysh : kNone;
+    case MOE_WS_BARRIER: return L.fbar;
     default: return kNone;
   }
 }
@@ -668,6 +678,11 @@ moe_status_t moe_layer_forward_timed(const moe_config_t* cfg, const moe_weights_
                     events);
 }
 
+int64_t moe_fused_set_spin_limit(int64_t polls) {
+  if (polls < 0) polls = kDefaultFusedSpinLimit;
+  return g_fused_spin_limit.exchange(polls);
+}
+
 moe_status_t moe_layer_forward_fused(const moe_config_t* cfg, const moe_weights_t* w,
                                      const void* x, void* out, int32_t* opt_counts,
                                      int32_t* opt_tie_counts, void* workspace,
@@ -721,6 +736,8 @@ moe_status_t moe_layer_forward_fused(const moe_config_t* cfg, const moe_weights_
   a.ysh = at<float>(ws, L.ysh);
   a.residual = nullptr;
   a.out = out;
+  a.bar = at<uint32_t>(ws, L.fbar);
+  a.spin_limit = g_fused_spin_limit.load();
   clear_stale_error();
   return hip_status(launch_fused_decode(a, static_cast<hipStream_t>(stream)));
 }

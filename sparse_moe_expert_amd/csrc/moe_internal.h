@@ -69,6 +69,7 @@ struct Layout {
   size_t y;             // [R, H] fp32  (routed expert outputs, sorted)
   size_t ysh;           // [S, T, H] fp32
   size_t xn;            // [T, H] act type: the normalised input of a block forward
+  size_t fbar;          // [2] uint32: the single-launch layer's barrier counter and status
   size_t total;
   int nchunks;
   int router_splits;    // >= 1
@@ -207,6 +208,8 @@ struct FusedArgs {
   const float* ysh;          // [S, T, H] fp32 (= dn.C2)
   const void* residual;      // null or [T, H] bf16
   void* out;                 // [T, H] bf16
+  uint32_t* bar;             // [2] in the workspace: barrier arrivals, status (1: a wait timed out)
+  long long spin_limit;      // polls per grid barrier before a block gives up
 };
 bool fused_decode_supported(TileShape gu, TileShape dn);
 hipError_t launch_fused_decode(const FusedArgs& a, hipStream_t st);

@@ -277,7 +277,9 @@ def test_workspace_offsets():
     assert moe.moe_workspace_offset(f8, moe.MOE_WS_H_SCALES) is not None
     s0 = moe.make_config(T=64, H=512, E=8, S=0, k=2, I=128)
     assert moe.moe_workspace_offset(s0, moe.MOE_WS_Y_SHARED) is None
-    assert moe.moe_workspace_offset(dec, 12) is None and moe.moe_workspace_offset(dec, -1) is None
+    bar = moe.moe_workspace_offset(dec, moe.MOE_WS_BARRIER)
+    assert bar is not None and bar % 256 == 0 and bar + 8 <= n
+    assert moe.moe_workspace_offset(dec, 13) is None and moe.moe_workspace_offset(dec, -1) is None
     assert moe.moe_workspace_offset(moe.make_config(T=1, H=100, E=8, S=1, k=2, I=128),
                                     moe.MOE_WS_H) is None
 

@@ -114,3 +114,36 @@ def test_fused_is_deterministic():
     a, _, _ = fused(lay)
     b, _, _ = fused(lay)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def barrier_words(lay):
+    off = moe.moe_workspace_offset(lay.ccfg, moe.MOE_WS_BARRIER)
+    return lay.workspace[off:off + 8].view(torch.int32).cpu().numpy()
+
+
+def test_fused_barrier_status_and_timeout():
+    """The grid barrier's bounded wait: after a completed launch the status
+    word is 0 and the arrival counter holds one arrival per block and barrier
+    (5 barriers); with a spin limit of 0 every block that finds blocks missing
+    gives up at its first poll and sets the status, and every other block
+    stops at its next barrier, so the launch still ends.  The next launch with
+    the default limit completes and gives the same output as before."""
+    cfg = small(T=64, E=64, k=8)
+    lay = DeviceLayer(cfg, generate(cfg))
+    ref, _, _ = fused(lay)
+    words = barrier_words(lay)
+    log(f"fused barrier words after a completed launch: {words.tolist()}")
+    assert words[1] == 0 and words[0] > 0 and words[0] % 5 == 0
+    prev = moe.moe_fused_set_spin_limit(0)
+    try:
+        log("fused launch with spin limit 0")
+        fused(lay)
+    finally:
+        moe.moe_fused_set_spin_limit(prev)
+    words = barrier_words(lay)
+    log(f"fused barrier words after the launch with spin limit 0: {words.tolist()}")
+    assert words[1] == 1
+    assert moe.moe_fused_set_spin_limit(-1) == prev  # the default restored
+    again, _, _ = fused(lay)
+    assert barrier_words(lay)[1] == 0
+    assert torch.equal(again.view(torch.int16), ref.view(torch.int16))
