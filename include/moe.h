@@ -192,8 +192,15 @@ size_t moe_workspace_size(const moe_config_t* cfg);
  *                                      chosen so that the block's largest |c|
  *                                      lies in [2^14, 2^15) (e = 0 for a block
  *                                      of zeros)
- *  MOE_WS_Y          fp32  [T*k, H]    routed expert outputs, sorted rows
- *  MOE_WS_Y_SHARED   fp32  [S, T, H]   shared expert outputs
+ *  MOE_WS_Y          fp32  [T*k, H]    routed expert outputs, sorted rows;
+ *                                      bf16 experts on the large-tile path:
+ *                                      fp16 codes, y = c * 2^e (MOE_WS_Y_EXP)
+ *  MOE_WS_Y_SHARED   fp32  [S, T, H]   shared expert outputs (fp16 codes as
+ *                                      MOE_WS_Y on the large-tile path)
+ *  MOE_WS_Y_EXP      int32 [T*k + S*T, ceil(H/256)]  large-tile path only:
+ *                                      exponents of y and y_shared per row of
+ *                                      the sorted row space and 256 columns,
+ *                                      as MOE_WS_H_EXP
  *  MOE_WS_BARRIER    uint32 [2]        moe_layer_forward_fused only: its grid
  *                                      barrier's arrival count, then a status
  *                                      word, 0 after a completed launch and
@@ -207,7 +214,8 @@ size_t moe_workspace_size(const moe_config_t* cfg);
 typedef enum {
   MOE_WS_TOPK_IDX = 0, MOE_WS_TOPK_W = 1, MOE_WS_COUNTS = 2, MOE_WS_OFFSETS = 3,
   MOE_WS_PERM = 4, MOE_WS_INV = 5, MOE_WS_H = 6, MOE_WS_H_SCALES = 7, MOE_WS_H_LO = 8,
-  MOE_WS_Y = 9, MOE_WS_Y_SHARED = 10, MOE_WS_H_EXP = 11, MOE_WS_BARRIER = 12
+  MOE_WS_Y = 9, MOE_WS_Y_SHARED = 10, MOE_WS_H_EXP = 11, MOE_WS_BARRIER = 12,
+  MOE_WS_Y_EXP = 13
 } moe_ws_part_t;
 size_t moe_workspace_offset(const moe_config_t* cfg, int32_t part);
 

@@ -20,7 +20,7 @@ MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 # moe_ws_part_t
 (MOE_WS_TOPK_IDX, MOE_WS_TOPK_W, MOE_WS_COUNTS, MOE_WS_OFFSETS, MOE_WS_PERM, MOE_WS_INV,
  MOE_WS_H, MOE_WS_H_SCALES, MOE_WS_H_LO, MOE_WS_Y, MOE_WS_Y_SHARED, MOE_WS_H_EXP,
- MOE_WS_BARRIER) = range(13)
+ MOE_WS_BARRIER, MOE_WS_Y_EXP) = range(14)
 WS_NONE = (1 << 64) - 1
 
 # every entry point of include/moe.h

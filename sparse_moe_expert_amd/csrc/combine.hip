@@ -18,9 +18,10 @@
 namespace moe {
 namespace {
 
-template <int OK>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
-                                                      const float* __restrict__ ysh,
+template <int OK, bool YF16>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
+                                                      const void* __restrict__ ysh,
+                                                      const int32_t* __restrict__ yexp,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ inv,
                                                       const void* __restrict__ residual,
@@ -32,7 +33,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int per = (H / static_cast<int>(gridDim.y) + 3) & ~3;
   const int c0 = static_cast<int>(blockIdx.y) * per;
   const int c1 = min(H, c0 + per);
-  combine_token<OK>(y, ysh, w, inv, residual, out, T, H, k, S, blockIdx.x, ws, rs, c0, c1);
+  combine_token<OK, YF16>(y, ysh, w, inv, residual, out, T, H, k, S, blockIdx.x, ws, rs, c0, c1,
+                          yexp);
 }
 
 // 16 lanes per 128-channel block, 8 channels per lane.
@@ -59,8 +61,7 @@ __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t* __r
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   }
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  amax = row16_fmax(amax);
   if (!on) return;
   const float scale = (amax == 0.f) ? 1.0f : amax / 448.0f;
   uint2 codes;
@@ -72,23 +73,28 @@ __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t* __r
 
 }  // namespace
 
-hipError_t launch_combine(int act_kind, const void* y, const void* ysh, const float* w,
-                          const int32_t* inv, const void* residual, void* out, int T, int H, int k,
-                          int S, hipStream_t st) {
+hipError_t launch_combine(int act_kind, const void* y, const void* ysh, const int32_t* yexp,
+                          const float* w, const int32_t* inv, const void* residual, void* out,
+                          int T, int H, int k, int S, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  const float* yf = static_cast<const float*>(y);
-  const float* yshf = static_cast<const float*>(ysh);
   // Small batches: split each token's columns over up to 4 blocks (at least
   // 1024 columns each) so that the launch has ~1024 blocks.  Measured at
   // T=256: 16.7 us with one block per token, 13.3 us split in 4.
   int parts = 1;
   while (parts < 4 && static_cast<long long>(T) * parts < 1024 && H / (2 * parts) >= 1024) parts *= 2;
-  if (act_kind == K_BF16)
-    hipLaunchKernelGGL(combine_kernel<K_BF16>, dim3(T, parts), dim3(256), 0, st, yf, yshf, w,
-                       inv, residual, out, T, H, k, S);
-  else
-    hipLaunchKernelGGL(combine_kernel<K_F32>, dim3(T, parts), dim3(256), 0, st, yf, yshf, w, inv,
+  const dim3 g(T, parts);
+  if (act_kind == K_BF16) {
+    if (yexp)
+      hipLaunchKernelGGL((combine_kernel<K_BF16, true>), g, dim3(256), 0, st, y, ysh, yexp, w, inv,
+                         residual, out, T, H, k, S);
+    else
+      hipLaunchKernelGGL((combine_kernel<K_BF16, false>), g, dim3(256), 0, st, y, ysh, yexp, w,
+                         inv, residual, out, T, H, k, S);
+  } else {
+    if (yexp) return hipErrorInvalidValue;  // fp32 layers keep fp32 y
+    hipLaunchKernelGGL((combine_kernel<K_F32, false>), g, dim3(256), 0, st, y, ysh, yexp, w, inv,
                        residual, out, T, H, k, S);
+  }
   return hipGetLastError();
 }
 

@@ -14,14 +14,35 @@ namespace moe {
 // kMaxTopK entries of LDS each.  Each output element is summed by one thread
 // in the fixed order (residual, shared experts, slots j ascending), so the
 // column split does not change the result.
-template <int OK>
-__device__ __forceinline__ void combine_token(const float* __restrict__ y,
-                                              const float* __restrict__ ysh,
+// YF16: y and ysh hold fp16 codes, value = code * 2^e with e from yexp
+// [T*k + S*T rows, ceil(H / kHBlock)] (row of the sorted row space).
+template <int OK, bool YF16 = false>
+__device__ __forceinline__ void combine_token(const void* __restrict__ y_,
+                                              const void* __restrict__ ysh_,
                                               const float* __restrict__ w,
                                               const int32_t* __restrict__ inv,
                                               const void* __restrict__ residual,
                                               void* __restrict__ out, int T, int H, int k, int S,
-                                              int t, float* ws, long long* rs, int c0, int c1) {
+                                              int t, float* ws, long long* rs, int c0, int c1,
+                                              const int32_t* __restrict__ yexp = nullptr) {
+  const int yeb = (H + kHBlock - 1) / kHBlock;
+  const long long R = static_cast<long long>(T) * k;
+  // 4 values of row `row` at column c (c % 4 == 0: one exponent block)
+  auto load4 = [&](const void* base, long long row, long long drow, int c) __attribute__((always_inline)) {
+    if constexpr (YF16) {
+      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+      const h4 u = __builtin_nontemporal_load(
+          reinterpret_cast<const h4*>(static_cast<const uint16_t*>(base) + drow * H + c));
+      const int e = yexp[row * yeb + c / kHBlock];
+      const h4 a = u, b = h4{u[2], u[3], u[2], u[3]};
+      return float4{ldexpf(static_cast<float>(a[0]), e), ldexpf(static_cast<float>(a[1]), e),
+                    ldexpf(static_cast<float>(b[0]), e), ldexpf(static_cast<float>(b[1]), e)};
+    } else {
+      const f32x4 vv = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + drow * H + c));
+      return float4{vv[0], vv[1], vv[2], vv[3]};
+    }
+  };
   if (threadIdx.x < k) {
     ws[threadIdx.x] = w[static_cast<long long>(t) * k + threadIdx.x];
     rs[threadIdx.x] = inv[static_cast<long long>(t) * k + threadIdx.x];
@@ -44,9 +65,8 @@ __device__ __forceinline__ void combine_token(const float* __restrict__ y,
       }
     }
     for (int s = 0; s < S; ++s) {
-      const f32x4 vv = __builtin_nontemporal_load(
-          reinterpret_cast<const f32x4*>(ysh + (static_cast<long long>(s) * T + t) * H + c));
-      const float4 v = float4{vv[0], vv[1], vv[2], vv[3]};
+      const long long srow = static_cast<long long>(s) * T + t;
+      const float4 v = load4(ysh_, R + srow, srow, c);
       acc.x += v.x;
       acc.y += v.y;
       acc.z += v.z;
@@ -56,8 +76,7 @@ __device__ __forceinline__ void combine_token(const float* __restrict__ y,
       const float wj = ws[j];
       // y is read exactly once: a nontemporal load keeps it from evicting
       // the rest of the stream from the caches (measured: combine 7% faster)
-      const f32x4 vv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + rs[j] * H + c));
-      const float4 v = float4{vv[0], vv[1], vv[2], vv[3]};
+      const float4 v = load4(y_, rs[j], rs[j], c);
       acc.x = fmaf(wj, v.x, acc.x);
       acc.y = fmaf(wj, v.y, acc.y);
       acc.z = fmaf(wj, v.z, acc.z);

@@ -378,8 +378,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmLaunch p) {
         v[i] = src[i];
         amax = fmaxf(amax, fabsf(v[i]));
       }
-#pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+      amax = row16_fmax(amax);
       const float scale = (amax == 0.f) ? 1.0f : amax / 448.0f;
       if (r < rows_here) {
         const long long row = row_begin + m0 + r;

@@ -290,8 +290,7 @@ __device__ __forceinline__ void tile_body(const GemmLaunch& p, const TileJob& jo
         v[i] = src[i];
         amax = fmaxf(amax, fabsf(v[i]));
       }
-#pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+      amax = row16_fmax(amax);
       const float scale = (amax == 0.f) ? 1.0f : amax / 448.0f;
       const int n = job.n0 + c8;
       if (r < job.rows_here && n < N) {

@@ -115,7 +115,7 @@ __device__ __forceinline__ half8 bf16x8_to_f16(const bf16x8& w) {
 // each row's blocks to the row's largest exponent while staging them, runs
 // fp16 MFMAs with the bf16 weights converted in registers, and scales the
 // row by 2^e in its epilogue.  erow: BM ints of LDS outside smem.
-template <bool DUAL, int MS, bool F16>
+template <bool DUAL, int MS, bool F16, bool YF16>
 __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, char* smem, int nk,
                                           int kt0, int* erow) {
   const int tid = threadIdx.x;
@@ -137,6 +137,7 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
   // that brings the block to the row's largest exponent e_row (LDS after the
   // A ring; each slice reads its block's entry before the slice barrier)
   constexpr bool A16 = F16 && !DUAL;
+  static_assert(!YF16 || A16, "fp16 y comes from the projection of fp16 h");
   uint32_t* mult_tab = reinterpret_cast<uint32_t*>(smem + U * A_SLOT);
   const int nb = p.exp_blocks;
   auto mult_of = [&](int kt) __attribute__((always_inline)) {
@@ -311,35 +312,49 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
     if constexpr (F16) {
       // per row: the 32 lanes of a half wave hold its 256 columns; the
       // block's exponent e puts its largest |h| * 2^-e in [2^14, 2^15)
-      static_assert(BM * 32 % THREADS == 0, "every lane takes part in each row's reduction");
-      for (int q = tid; q < BM * 32; q += THREADS) {
-        const int r = q >> 5;
-        const int c8 = (q & 31) * 8;
-        const int n = job.n0 + c8;
-        const float* src = Cs + r * LDC + c8;
-        float v[8];
-        float amax = 0.f;
+      // Rows go in batches of RB per wave, so that their LDS reads, reductions
+      // and stores overlap (one workgroup per CU leaves little else to hide
+      // each row's latency chain).
+      constexpr int ITER = BM * 32 / THREADS, RB = 4;
+      static_assert(BM * 32 % THREADS == 0 && ITER % RB == 0, "every lane takes part in each row's reduction");
+      for (int it = 0; it < ITER; it += RB) {
+        float v[RB][8], amax[RB];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          v[i] = src[i];
-          if (n + i < N) amax = fmaxf(amax, fabsf(v[i]));
+        for (int j = 0; j < RB; ++j) {
+          const int q = tid + (it + j) * THREADS;
+          const int n = job.n0 + (q & 31) * 8;
+          const float* src = Cs + (q >> 5) * LDC + (q & 31) * 8;
+          amax[j] = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            v[j][i] = src[i];
+            if (n + i < N) amax[j] = fmaxf(amax[j], fabsf(v[j][i]));
+          }
         }
 #pragma unroll
-        for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-        // amax = f * 2^x, f in [0.5, 1): e = x - 15; zeros (and inf/NaN) keep e = 0
-        const int e = (amax > 0.f && amax <= 3.402823466e38f) ? __builtin_amdgcn_frexp_expf(amax) - 15 : 0;
-        if (r >= job.rows_here || n >= N) continue;
-        const long long row = job.row_begin + job.m0 + r;
-        char* dst = gemm_out_row<2>(p, row);
-        if (c8 == 0) p.c_exp[row * p.exp_blocks + job.n0 / kHBlock] = e;
-        if (n + 8 <= N) {
-          half8 o;
+        for (int j = 0; j < RB; ++j) amax[j] = half_wave_fmax_nonneg(amax[j]);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) o[i] = static_cast<_Float16>(ldexpf(v[i], -e));
-          *reinterpret_cast<half8*>(dst + static_cast<long long>(n) * 2) = o;
-        } else {
-          for (int i = 0; n + i < N; ++i)
-            reinterpret_cast<_Float16*>(dst)[n + i] = static_cast<_Float16>(ldexpf(v[i], -e));
+        for (int j = 0; j < RB; ++j) {
+          const int q = tid + (it + j) * THREADS;
+          const int r = q >> 5;
+          const int c8 = (q & 31) * 8;
+          const int n = job.n0 + c8;
+          // amax = f * 2^x, f in [0.5, 1): e = x - 15; zeros (and inf/NaN) keep e = 0
+          const int e = (amax[j] > 0.f && amax[j] <= 3.402823466e38f) ? __builtin_amdgcn_frexp_expf(amax[j]) - 15 : 0;
+          if (r >= job.rows_here || n >= N) continue;
+          const long long row = job.row_begin + job.m0 + r;
+          char* dst = gemm_out_row<2>(p, row);
+          if (c8 == 0) p.c_exp[row * p.c_exp_blocks + job.n0 / kHBlock] = e;
+          if (n + 8 <= N) {
+            half8 o;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = static_cast<_Float16>(ldexpf(v[j][i], -e));
+            *reinterpret_cast<half8*>(dst + static_cast<long long>(n) * 2) = o;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              if (n + i < N) reinterpret_cast<_Float16*>(dst)[n + i] = static_cast<_Float16>(ldexpf(v[j][i], -e));
+          }
         }
       }
       return;
@@ -379,17 +394,71 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
               Cs[(m * 16 + lgrp * 4 + i) * LDC + (wave & 3) * 64 + t * 16 + lrow] = acc[m][t][i];
       }
       __syncthreads();
+      if constexpr (YF16) {
+        // scaled fp16 y: one wave holds a row's 256 columns of this pass, one
+        // exponent block; e puts the block's largest |y| * 2^-e in
+        // [2^14, 2^15) (0 for a block of zeros).  Rows go in batches of RB
+        // per wave so that their latency chains overlap.
+        constexpr int ITER = BM * 64 / THREADS, RB = 4;
+        static_assert(BM * 64 % THREADS == 0 && ITER % RB == 0, "every lane takes part in each row's reduction");
+        for (int it = 0; it < ITER; it += RB) {
+          f32x4 o[RB];
+          float amax[RB];
+#pragma unroll
+          for (int j = 0; j < RB; ++j) {
+            const int q = tid + (it + j) * THREADS;
+            const int r = q >> 6;
+            const int n = job.n0 + half * 256 + (q & 63) * 4;
+            const float* src = Cs + r * LDC + (q & 63) * 4;
+            const int ea = erow[r];
+            o[j] = f32x4{ldexpf(src[0], ea), ldexpf(src[1], ea), ldexpf(src[2], ea), ldexpf(src[3], ea)};
+            amax[j] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (n + i < N) amax[j] = fmaxf(amax[j], fabsf(o[j][i]));
+          }
+#pragma unroll
+          for (int j = 0; j < RB; ++j) amax[j] = wave_fmax_nonneg(amax[j]);
+#pragma unroll
+          for (int j = 0; j < RB; ++j) {
+            const int q = tid + (it + j) * THREADS;
+            const int r = q >> 6;
+            const int c4 = (q & 63) * 4;
+            const int n = job.n0 + half * 256 + c4;
+            const int e =
+                (amax[j] > 0.f && amax[j] <= 3.402823466e38f) ? __builtin_amdgcn_frexp_expf(amax[j]) - 15 : 0;
+            if (r >= job.rows_here || n >= N) continue;
+            const long long row = job.row_begin + job.m0 + r;
+            _Float16* dst = reinterpret_cast<_Float16*>(gemm_out_row<2>(p, row));
+            if (c4 == 0) p.c_exp[row * p.c_exp_blocks + (job.n0 + half * 256) / kHBlock] = e;
+            if (n + 4 <= N) {
+              typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+              const h4 hv = h4{static_cast<_Float16>(ldexpf(o[j][0], -e)), static_cast<_Float16>(ldexpf(o[j][1], -e)),
+                               static_cast<_Float16>(ldexpf(o[j][2], -e)), static_cast<_Float16>(ldexpf(o[j][3], -e))};
+              // y is read once, by the combine
+              typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+              __builtin_nontemporal_store(__builtin_bit_cast(u32x2, hv), reinterpret_cast<u32x2*>(dst + n));
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (n + i < N) dst[n + i] = static_cast<_Float16>(ldexpf(o[j][i], -e));
+            }
+          }
+        }
+        __syncthreads();
+        continue;
+      }
       for (int q = tid; q < BM * 64; q += THREADS) {
         const int r = q >> 6;
         const int c4 = (q & 63) * 4;
         const int n = job.n0 + half * 256 + c4;
+        const float* src = Cs + r * LDC + c4;
+        const int ea = A16 ? erow[r] : 0;  // A16: the row's exponent
+        const f32x4 o = A16 ? f32x4{ldexpf(src[0], ea), ldexpf(src[1], ea), ldexpf(src[2], ea),
+                                    ldexpf(src[3], ea)}
+                            : f32x4{src[0], src[1], src[2], src[3]};
         if (r < job.rows_here && n < N) {
-          const float* src = Cs + r * LDC + c4;
           float* dst = reinterpret_cast<float*>(gemm_out_row<4>(p, job.row_begin + job.m0 + r));
-          const int e = A16 ? erow[r] : 0;  // A16: the row's exponent
-          const f32x4 o = A16 ? f32x4{ldexpf(src[0], e), ldexpf(src[1], e), ldexpf(src[2], e),
-                                      ldexpf(src[3], e)}
-                              : f32x4{src[0], src[1], src[2], src[3]};
           if (n + 4 <= N) {
             // y is read once, by the combine: nontemporal stores keep it from
             // evicting the weight slices the other m-tiles still read from L2
@@ -404,7 +473,7 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
   }
 }
 
-template <bool DUAL, bool PARTN, bool F16>
+template <bool DUAL, bool PARTN, bool F16, bool YF16>
 __global__ __launch_bounds__(THREADS, 1) void gemm_prefill_kernel(GemmLaunch p) {
   constexpr int BN = DUAL ? 256 : 512;  // output columns per block
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
@@ -432,11 +501,11 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_prefill_kernel(GemmLaunch p) 
   const bool n_act = DUAL ? (!PARTN || job.n0 + wave * 32 < N) : job.n0 + wave * 64 < N;
   const int ms = n_act ? min(4, (job.rows_here + 31) >> 5) * 2 : 0;
   switch (ms) {
-    case 8: tile_body<DUAL, 8, F16>(p, job, smem, nk, kt0, erow); break;
-    case 6: tile_body<DUAL, 6, F16>(p, job, smem, nk, kt0, erow); break;
-    case 4: tile_body<DUAL, 4, F16>(p, job, smem, nk, kt0, erow); break;
-    case 2: tile_body<DUAL, 2, F16>(p, job, smem, nk, kt0, erow); break;
-    default: tile_body<DUAL, 0, F16>(p, job, smem, nk, kt0, erow); break;
+    case 8: tile_body<DUAL, 8, F16, YF16>(p, job, smem, nk, kt0, erow); break;
+    case 6: tile_body<DUAL, 6, F16, YF16>(p, job, smem, nk, kt0, erow); break;
+    case 4: tile_body<DUAL, 4, F16, YF16>(p, job, smem, nk, kt0, erow); break;
+    case 2: tile_body<DUAL, 2, F16, YF16>(p, job, smem, nk, kt0, erow); break;
+    default: tile_body<DUAL, 0, F16, YF16>(p, job, smem, nk, kt0, erow); break;
   }
 }
 
@@ -454,23 +523,26 @@ hipError_t launch_prefill(const GemmLaunch& g, hipStream_t st) {
   const long long grid = ((total + 7) / 8) * 8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 gd(static_cast<unsigned>(grid), static_cast<unsigned>(splits));
+  // scaled fp16: gate/up writes h that way (c_exp); the projection reads A
+  // = h that way (a_exp) and, in the layer, writes y that way too (c_exp)
   const bool f16 = DUAL ? g.c_exp != nullptr : g.a_exp != nullptr;
-  if (f16) {
-    // one exponent per 256 columns of h: gate/up tiles are 256 wide; the
-    // projection's shift table has room for kMaxHBlocks blocks per row
-    if (g.exp_blocks != ((DUAL ? g.N : g.K) + kHBlock - 1) / kHBlock || g.exp_blocks > kMaxHBlocks)
-      return hipErrorInvalidValue;
-    if (!DUAL && g.k_splits > 1) return hipErrorInvalidValue;
-  }
+  const bool yf16 = !DUAL && g.c_exp != nullptr;
+  if (g.a_exp && (g.exp_blocks != (g.K + kHBlock - 1) / kHBlock || g.exp_blocks > kMaxHBlocks ||
+                  g.k_splits > 1))
+    return hipErrorInvalidValue;
+  if (g.c_exp && g.c_exp_blocks != (g.N + kHBlock - 1) / kHBlock) return hipErrorInvalidValue;
+  if (yf16 && !f16) return hipErrorInvalidValue;  // fp16 y only from fp16 h
   if (DUAL && g.N % BN != 0) {
     if (f16)
-      hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, true, true>), gd, dim3(THREADS), 0, st, g);
+      hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, true, true, false>), gd, dim3(THREADS), 0, st, g);
     else
-      hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, true, false>), gd, dim3(THREADS), 0, st, g);
+      hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, true, false, false>), gd, dim3(THREADS), 0, st, g);
+  } else if (yf16) {
+    hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, false, true, !DUAL>), gd, dim3(THREADS), 0, st, g);
   } else if (f16) {
-    hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, false, true>), gd, dim3(THREADS), 0, st, g);
+    hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, false, true, false>), gd, dim3(THREADS), 0, st, g);
   } else {
-    hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, false, false>), gd, dim3(THREADS), 0, st, g);
+    hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, false, false, false>), gd, dim3(THREADS), 0, st, g);
   }
   return hipGetLastError();
 }

@@ -208,7 +208,7 @@ GemmLaunch gate_up_launch(const moe_config_t& c, const Layout& L, const void* x,
   g.c_scale = fp8 ? at<float>(ws, L.hs) : nullptr;
   g.C_lo = L.h_split ? at<char>(ws, L.hlo) : nullptr;
   g.c_exp = L.h_f16 ? at<int32_t>(ws, L.hexp) : nullptr;
-  g.exp_blocks = (c.I + kHBlock - 1) / kHBlock;
+  g.c_exp_blocks = (c.I + kHBlock - 1) / kHBlock;
   g.w_tiled = c.expert_layout == MOE_LAYOUT_TILED;
   return g;
 }
@@ -227,7 +227,7 @@ hipError_t run_gate_up(const moe_config_t& c, const Layout& L, const void* x, co
 }
 
 hipError_t run_down(const moe_config_t& c, const Layout& L, void* y_sorted, void* y_shared,
-                    void* ws, hipStream_t st);
+                    void* ws, hipStream_t st, bool y_f16 = false);
 
 hipError_t record(void* const* events, int i, hipStream_t st) {
   if (!events) return hipSuccess;
@@ -282,10 +282,12 @@ hipError_t layer_run(const moe_config_t& c, const moe_weights_t* w, const void* 
   if (e == hipSuccess) e = record(events, 3, st);
   if (e == hipSuccess) e = run_gate_up_gemm(c, L, x, perm, ws, st);
   if (e == hipSuccess) e = record(events, 4, st);
-  if (e == hipSuccess) e = run_down(c, L, y, ysh, ws, st);
+  // inside the layer y stays in the workspace: scaled fp16 on the large-tile path
+  if (e == hipSuccess) e = run_down(c, L, y, ysh, ws, st, L.h_f16);
   if (e == hipSuccess) e = record(events, 5, st);
   if (e == hipSuccess)
-    e = launch_combine(act_kind(c), y, ysh, tw, inv, residual, out, c.T, c.H, c.k, c.S, st);
+    e = launch_combine(act_kind(c), y, ysh, L.h_f16 ? at<int32_t>(ws, L.yexp) : nullptr, tw, inv,
+                       residual, out, c.T, c.H, c.k, c.S, st);
   if (e == hipSuccess) e = record(events, 6, st);
   return e;
 }
@@ -300,8 +302,10 @@ moe_status_t layer_impl(const moe_config_t* cfg, const moe_weights_t* w, const v
                               static_cast<hipStream_t>(stream), events));
 }
 
+// y_f16 (the layer's own y, large-tile path): y and y_sh as scaled fp16 with
+// exponents in the workspace (yexp); otherwise fp32 into the given buffers
 GemmLaunch down_launch(const moe_config_t& c, const Layout& L, void* y_sorted, void* y_shared,
-                       void* ws) {
+                       void* ws, bool y_f16 = false) {
   const bool fp8 = is_fp8(c);
   GemmLaunch g{};
   g.groups = at<GroupDesc>(ws, L.groups);
@@ -326,13 +330,16 @@ GemmLaunch down_launch(const moe_config_t& c, const Layout& L, void* y_sorted, v
   g.A_lo = L.h_split ? at<char>(ws, L.hlo) : nullptr;
   g.a_exp = L.h_f16 ? at<int32_t>(ws, L.hexp) : nullptr;
   g.exp_blocks = (c.I + kHBlock - 1) / kHBlock;
+  g.c_exp = (y_f16 && L.h_f16) ? at<int32_t>(ws, L.yexp) : nullptr;
+  g.c_exp_blocks = (c.H + kHBlock - 1) / kHBlock;
   g.w_tiled = c.expert_layout == MOE_LAYOUT_TILED;
   return g;
 }
 
 hipError_t run_down(const moe_config_t& c, const Layout& L, void* y_sorted, void* y_shared,
-                    void* ws, hipStream_t st) {
-  return launch_gemm(expert_kind(c), K_F32, L.dn, down_launch(c, L, y_sorted, y_shared, ws), st);
+                    void* ws, hipStream_t st, bool y_f16) {
+  return launch_gemm(expert_kind(c), K_F32, L.dn, down_launch(c, L, y_sorted, y_shared, ws, y_f16),
+                     st);
 }
 
 // Device address of `scratch` on the current device, looked up once per
@@ -473,8 +480,10 @@ Layout make_layout(const moe_config_t& c) {
   L.hlo = take(L.h_split ? rows_all * I * 2 : 0);
   L.hexp = take(L.h_f16 ? rows_all * ((I + kHBlock - 1) / kHBlock) * 4 : 0);
   L.hs = take(fp8 ? rows_all * (I / kQBlock) * 4 : 0);
-  L.y = take(R * H * 4);        // fp32: rounded once, in the combine
-  L.ysh = take(S * T * H * 4);
+  // fp32 (rounded once, in the combine), or scaled fp16 on the large-tile path
+  L.y = take(R * H * (L.h_f16 ? 2 : 4));
+  L.ysh = take(S * T * H * (L.h_f16 ? 2 : 4));
+  L.yexp = take(L.h_f16 ? rows_all * ((H + kHBlock - 1) / kHBlock) * 4 : 0);
   L.xn = take(T * H * asz);
   L.fbar = take(8);
   L.total = off;
@@ -526,6 +535,7 @@ size_t moe_workspace_offset(const moe_config_t* cfg, int32_t part) {
     case MOE_WS_Y: return L.y;
     case MOE_WS_Y_SHARED: return cfg->S > 0 ? L.ysh : kNone;
     case MOE_WS_BARRIER: return L.fbar;
+    case MOE_WS_Y_EXP: return L.h_f16 ? L.yexp : kNone;
     default: return kNone;
   }
 }
@@ -629,7 +639,7 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y_sorted, const vo
   if (cfg->S > 0 && (!y_shared || !aligned16(y_shared))) return MOE_ERR_INVALID_ARG;
   const moe_config_t& c = *cfg;
   clear_stale_error();
-  return hip_status(launch_combine(act_kind(c), y_sorted, y_shared, topk_w, inv, nullptr, out,
+  return hip_status(launch_combine(act_kind(c), y_sorted, y_shared, nullptr, topk_w, inv, nullptr, out,
                                    c.T, c.H, c.k, c.S, static_cast<hipStream_t>(stream)));
 }
 

@@ -65,6 +65,7 @@ struct Layout {
   size_t h;             // [R + S*T, I] act type, or e4m3 codes (FP8)
   size_t hlo;           // bf16 h_split: [R + S*T, I] bf16 residue h - bf16(h)
   size_t hexp;          // bf16 h_f16: [R + S*T, ceil(I / kHBlock)] int32 block exponents
+  size_t yexp;          // bf16 h_f16: [R + S*T, ceil(H / kHBlock)] int32 exponents of y, y_sh
   size_t hs;            // FP8: [R + S*T, I/128] fp32 scales
   size_t y;             // [R, H] fp32  (routed expert outputs, sorted)
   size_t ysh;           // [S, T, H] fp32
@@ -137,11 +138,14 @@ struct GemmLaunch {
   // with the stride and row mapping of A
   void* C_lo;
   const void* A_lo;
-  // scaled fp16 h (large-tile kernel only; null = not used): the gate/up GEMM
-  // stores v * 2^-e in fp16, e per row and block of kHBlock h columns chosen
-  // so that the block's largest |v| * 2^-e lies in [2^14, 2^15), with e in
-  // c_exp [rows, exp_blocks]; the down GEMM reads A that way through a_exp
+  // scaled fp16 (large-tile kernel only; null = not used): an output v is
+  // stored as fp16 v * 2^-e, e per row and block of kHBlock columns chosen so
+  // that the block's largest |v| * 2^-e lies in [2^14, 2^15), with e in
+  // c_exp [rows of the sorted row space, c_exp_blocks] (gate/up: h; down in
+  // the layer: y); the down GEMM reads A = h that way through a_exp
+  // [rows, exp_blocks]
   int32_t* c_exp;
+  int c_exp_blocks;
   const int32_t* a_exp;
   int exp_blocks;
   // split K (generic kernel, fp32 output only): block y computes the K range
@@ -248,8 +252,11 @@ hipError_t launch_quant_rows_fp8(const uint16_t* x_bf16, int rows, int cols, uin
                                  float* scales, hipStream_t st);
 
 // residual: null, or [T, H] of the act kind, added first (block forward)
-hipError_t launch_combine(int act_kind, const void* y, const void* ysh, const float* w,
-                          const int32_t* inv, const void* residual, void* out, int T, int H, int k,
-                          int S, hipStream_t st);
+// y, ysh fp32; or, with yexp (non-null), fp16 codes scaled per row and
+// kHBlock columns (exponents [T*k + S*T, ceil(H / kHBlock)], rows of the
+// sorted row space)
+hipError_t launch_combine(int act_kind, const void* y, const void* ysh, const int32_t* yexp,
+                          const float* w, const int32_t* inv, const void* residual, void* out,
+                          int T, int H, int k, int S, hipStream_t st);
 
 }  // namespace moe

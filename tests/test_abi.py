@@ -112,10 +112,10 @@ def test_workspace_size_covers_buffers():
     n = moe.moe_workspace_size(c)
     R = 16384 * 8
     # h (fp16 codes) and its block exponents (6 per row) + y_sorted and
-    # y_shared (fp32) + router logits (fp32, K split 2 ways at this T) + the
-    # normalised block input (bf16)
-    need = ((R + 16384) * 1536 * 2 + (R + 16384) * 6 * 4 + R * 5120 * 4 + 16384 * 5120 * 4
-            + 2 * 16384 * 256 * 4 + 16384 * 5120 * 2)
+    # y_shared (fp16 codes) and their exponents (20 per row) + router logits
+    # (fp32, K split 2 ways at this T) + the normalised block input (bf16)
+    need = ((R + 16384) * 1536 * 2 + (R + 16384) * 6 * 4 + R * 5120 * 2 + 16384 * 5120 * 2
+            + (R + 16384) * 20 * 4 + 2 * 16384 * 256 * 4 + 16384 * 5120 * 2)
     assert need <= n < need * 1.05
 
 
@@ -248,6 +248,9 @@ def test_pack_validation():
     assert call(P, A, B, 1 << 62, 16, 128, moe.MOE_BF16, None) == moe.MOE_ERR_INVALID_ARG
 
 
+MAX_PART = 13
+
+
 def test_workspace_offsets():
     """moe_workspace_offset: every part lies inside the workspace, in the order
     of the carve-out; h's bf16 residue exists only where the down GEMM streams
@@ -279,7 +282,10 @@ def test_workspace_offsets():
     assert moe.moe_workspace_offset(s0, moe.MOE_WS_Y_SHARED) is None
     bar = moe.moe_workspace_offset(dec, moe.MOE_WS_BARRIER)
     assert bar is not None and bar % 256 == 0 and bar + 8 <= n
-    assert moe.moe_workspace_offset(dec, 13) is None and moe.moe_workspace_offset(dec, -1) is None
+    assert moe.moe_workspace_offset(dec, MAX_PART + 1) is None and moe.moe_workspace_offset(dec, -1) is None
+    assert moe.moe_workspace_offset(dec, moe.MOE_WS_Y_EXP) is None
+    ye = moe.moe_workspace_offset(big, moe.MOE_WS_Y_EXP)
+    assert ye is not None and ye + (16384 * 9) * 20 * 4 <= moe.moe_workspace_size(big)
     assert moe.moe_workspace_offset(moe.make_config(T=1, H=100, E=8, S=1, k=2, I=128),
                                     moe.MOE_WS_H) is None
 

@@ -343,9 +343,6 @@ def test_layer_intermediates(case):
     np.testing.assert_array_equal(offs, d.offsets)
     rows = np.arange(rows_all)
     h_ref, grp, tok = oracle_h_rows(cfg, inp, perm, offs, rows)
-    y_gpu = ws_part(moe, c, ws, moe.MOE_WS_Y, torch.float32, (R, cfg.H)).cpu().numpy()
-    ysh_gpu = (ws_part(moe, c, ws, moe.MOE_WS_Y_SHARED, torch.float32, (cfg.S, cfg.T, cfg.H))
-               .cpu().numpy() if cfg.S else np.zeros((0, cfg.T, cfg.H)))
     W = oracle.Weights(cfg, inp)
     if cfg.expert == "bf16":
         split = moe.moe_workspace_offset(c, moe.MOE_WS_H_LO) is not None
@@ -373,7 +370,36 @@ def test_layer_intermediates(case):
         log(f"intermediates {case}: h {'two bf16 terms' if split else 'scaled fp16'}; max (|Δh| - "
             f"rounding)/rms(h) = {max(excess.max(), 0) / oracle.rms(h_ref):.3e}")
         assert excess.max() <= 1e-5 * oracle.rms(h_ref)
+        if split:
+            return
+        # y in the same scaled fp16 form (exponents per row and 256 output
+        # columns), against y recomputed in fp64 from the GPU's own h: one
+        # fp16 rounding of y plus 1e-4 rms(y) for the fp32 sums and for h
+        # brought to one exponent per row before the MFMAs.
+        nby = -(-cfg.H // 256)
+        yc = np.concatenate([
+            ws_part(moe, c, ws, moe.MOE_WS_Y, torch.float16, (R, cfg.H)).cpu().numpy(),
+            (ws_part(moe, c, ws, moe.MOE_WS_Y_SHARED, torch.float16, (cfg.S * cfg.T, cfg.H))
+             .cpu().numpy() if cfg.S else np.zeros((0, cfg.H), np.float16))]).astype(np.float64)
+        yex = ws_part(moe, c, ws, moe.MOE_WS_Y_EXP, torch.int32, (rows_all, nby)).cpu().numpy()
+        yex_col = np.repeat(yex, 256, axis=1)[:, :cfg.H].astype(np.float64)
+        y_gpu = yc * np.exp2(yex_col)
+        for b in range(nby):
+            amax = np.abs(yc[:, 256 * b:256 * (b + 1)]).max(axis=1)
+            ok = ((amax >= 2.0 ** 14) & (amax <= 2.0 ** 15)) | ((amax == 0) & (yex[:, b] == 0))
+            assert ok.all(), f"{case}: y block {b} codes out of [2^14, 2^15]: {amax[~ok][:4]}"
+        y_ref = np.zeros((rows_all, cfg.H))
+        for g in np.unique(grp):
+            sel = np.nonzero(grp == g)[0]
+            y_ref[sel] = h_gpu[sel] @ W.expert(int(g))[2].T
+        y_excess = np.abs(y_gpu - y_ref) - 2.0 ** -11 * np.abs(y_ref) - 2.0 ** -25 * np.exp2(yex_col)
+        log(f"intermediates {case}: y scaled fp16; max (|Δy| - rounding)/rms(y) = "
+            f"{max(y_excess.max(), 0) / oracle.rms(y_ref):.3e}")
+        assert y_excess.max() <= 1e-4 * oracle.rms(y_ref)
         return
+    y_gpu = ws_part(moe, c, ws, moe.MOE_WS_Y, torch.float32, (R, cfg.H)).cpu().numpy()
+    ysh_gpu = (ws_part(moe, c, ws, moe.MOE_WS_Y_SHARED, torch.float32, (cfg.S, cfg.T, cfg.H))
+               .cpu().numpy() if cfg.S else np.zeros((0, cfg.T, cfg.H)))
     # fp8
     codes = ws_part(moe, c, ws, moe.MOE_WS_H, torch.uint8, (rows_all, cfg.I)).cpu().numpy()
     scales = ws_part(moe, c, ws, moe.MOE_WS_H_SCALES, torch.float32,
