@@ -115,9 +115,11 @@ __device__ __forceinline__ half8 bf16x8_to_f16(const bf16x8& w) {
 // each row's blocks to the row's largest exponent while staging them, runs
 // fp16 MFMAs with the bf16 weights converted in registers, and scales the
 // row by 2^e in its epilogue.  erow: BM ints of LDS outside smem.
+// YF16 (projection of fp16 h): y leaves as fp16 codes with exponents per row
+// and 256 columns (c_exp); wmax: BM x WAVES floats of LDS for the row maxima.
 template <bool DUAL, int MS, bool F16, bool YF16>
 __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, char* smem, int nk,
-                                          int kt0, int* erow) {
+                                          int kt0, int* erow, float* wmax) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -137,6 +139,10 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
   // that brings the block to the row's largest exponent e_row (LDS after the
   // A ring; each slice reads its block's entry before the slice barrier)
   constexpr bool A16 = F16 && !DUAL;
+  // scaled fp16 outputs (h of gate/up, y of the projection): weights as the
+  // first MFMA operand, so that the accumulators hold the output transposed
+  // (4 consecutive output columns of one token row per lane)
+  constexpr bool TRN = (DUAL && F16) || YF16;
   static_assert(!YF16 || A16, "fp16 y comes from the projection of fp16 h");
   uint32_t* mult_tab = reinterpret_cast<uint32_t*>(smem + U * A_SLOT);
   const int nb = p.exp_blocks;
@@ -238,7 +244,8 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
       for (int m = 0; m < MS; ++m)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], b_ring[R][t], acc[m][t], 0, 0, 0);
+          acc[m][t] = TRN ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(b_ring[R][t], af[m], acc[m][t], 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], b_ring[R][t], acc[m][t], 0, 0, 0);
       // instruction order: all fragment reads, the LDS write of the next
       // slice, then the MFMAs with the five global loads spread among them
       __builtin_amdgcn_sched_group_barrier(0x100, MS, 0);  // DS read
@@ -263,7 +270,8 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
         const half8 bf = bf16x8_to_f16(b_ring[R][t]);
 #pragma unroll
         for (int m = 0; m < MS; ++m)
-          acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[m], bf, acc[m][t], 0, 0, 0);
+          acc[m][t] = TRN ? __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, af[m], acc[m][t], 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_16x16x32_f16(af[m], bf, acc[m][t], 0, 0, 0);
       }
       // instruction order: fragment reads, the LDS write of the next slice,
       // then per weight tile its conversion (12 VALU) and its MS MFMAs, the
@@ -298,7 +306,80 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
   float* Cs = reinterpret_cast<float*>(smem);
   const int lrow = lane & 15;
   const int lgrp = lane >> 4;
-  if constexpr (DUAL) {
+  if constexpr (DUAL && F16) {
+    // h = SiLU(g) * u from the transposed accumulators: lane l, element i ->
+    // h column 32 wave + 16 t + 4 (l / 16) + i of the tile (gate tile t =
+    // 0, 1, its up rows in tile t + 2), token row 16 m + l % 16.  The tile's
+    // 256 columns are one exponent block: e puts the row's largest
+    // |h| * 2^-e in [2^14, 2^15) (0 for a row of zeros).  Weight rows past N
+    // repeat row N - 1, so their columns do not change the maximum.
+    float rm[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      float v = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[m][t][i] = silu_mul(acc[m][t][i], acc[m][t + 2][i]);
+          v = fmaxf(v, fabsf(acc[m][t][i]));
+        }
+      rm[m] = v;
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) rm[m] = fmaxf(rm[m], __shfl_xor(rm[m], 16, 64));
+#pragma unroll
+    for (int m = 0; m < 8; ++m) rm[m] = fmaxf(rm[m], __shfl_xor(rm[m], 32, 64));
+    if (lgrp == 0) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) wmax[(m * 16 + lrow) * WAVES + wave] = rm[m];
+    }
+    __syncthreads();
+    // codes into LDS, rows of 256 fp16 at a 528-byte stride (8-byte writes
+    // of the 64 lanes fall on distinct banks)
+    constexpr int HROW = 2 * kHBlock + 16;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int r = m * 16 + lrow;
+      const f32x4 q0 = *reinterpret_cast<const f32x4*>(wmax + r * WAVES);
+      const f32x4 q1 = *reinterpret_cast<const f32x4*>(wmax + r * WAVES + 4);
+      const float amax = fmaxf(fmaxf(fmaxf(q0[0], q0[1]), fmaxf(q0[2], q0[3])),
+                               fmaxf(fmaxf(q1[0], q1[1]), fmaxf(q1[2], q1[3])));
+      const bool scaled = amax > 0.f && amax <= 3.402823466e38f;
+      const int x = scaled ? __builtin_amdgcn_frexp_expf(amax) : 15;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        const h4 c = h4{static_cast<_Float16>(ldexpf(acc[m][t][0], 15 - x)),
+                        static_cast<_Float16>(ldexpf(acc[m][t][1], 15 - x)),
+                        static_cast<_Float16>(ldexpf(acc[m][t][2], 15 - x)),
+                        static_cast<_Float16>(ldexpf(acc[m][t][3], 15 - x))};
+        *reinterpret_cast<h4*>(smem + r * HROW + (wave * 32 + t * 16 + lgrp * 4) * 2) = c;
+      }
+      if (wave == 0 && lgrp == 0 && r < job.rows_here)
+        p.c_exp[(job.row_begin + job.m0 + r) * static_cast<long long>(p.c_exp_blocks) + job.n0 / kHBlock] =
+            scaled ? x - 15 : 0;
+    }
+    __syncthreads();
+    // rows out: half a wave per row (256 columns, 512 bytes)
+#pragma unroll
+    for (int j = 0; j < BM / WAVES / 2; ++j) {
+      const int r = wave * (BM / WAVES) + 2 * j + (lane >> 5);
+      const int c8 = (lane & 31) * 8;
+      const int n = job.n0 + c8;
+      if (r < job.rows_here && n < N) {
+        const half8 v = *reinterpret_cast<const half8*>(smem + r * HROW + c8 * 2);
+        _Float16* dst = reinterpret_cast<_Float16*>(gemm_out_row<2>(p, job.row_begin + job.m0 + r));
+        if (n + 8 <= N) {
+          *reinterpret_cast<half8*>(dst + n) = v;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (n + i < N) dst[n + i] = v[i];
+        }
+      }
+    }
+  } else if constexpr (DUAL) {
     // h = SiLU(g) * u into Cs[row][h column]; wave w owns h columns [32w, +32)
 #pragma unroll
     for (int m = 0; m < MS; ++m)
@@ -309,56 +390,6 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
           Cs[(m * 16 + lgrp * 4 + i) * LDC + wave * 32 + t * 16 + lrow] =
               silu_mul(acc[m][t][i], acc[m][t + 2][i]);
     __syncthreads();
-    if constexpr (F16) {
-      // per row: the 32 lanes of a half wave hold its 256 columns; the
-      // block's exponent e puts its largest |h| * 2^-e in [2^14, 2^15)
-      // Rows go in batches of RB per wave, so that their LDS reads, reductions
-      // and stores overlap (one workgroup per CU leaves little else to hide
-      // each row's latency chain).
-      constexpr int ITER = BM * 32 / THREADS, RB = 4;
-      static_assert(BM * 32 % THREADS == 0 && ITER % RB == 0, "every lane takes part in each row's reduction");
-      for (int it = 0; it < ITER; it += RB) {
-        float v[RB][8], amax[RB];
-#pragma unroll
-        for (int j = 0; j < RB; ++j) {
-          const int q = tid + (it + j) * THREADS;
-          const int n = job.n0 + (q & 31) * 8;
-          const float* src = Cs + (q >> 5) * LDC + (q & 31) * 8;
-          amax[j] = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            v[j][i] = src[i];
-            if (n + i < N) amax[j] = fmaxf(amax[j], fabsf(v[j][i]));
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < RB; ++j) amax[j] = half_wave_fmax_nonneg(amax[j]);
-#pragma unroll
-        for (int j = 0; j < RB; ++j) {
-          const int q = tid + (it + j) * THREADS;
-          const int r = q >> 5;
-          const int c8 = (q & 31) * 8;
-          const int n = job.n0 + c8;
-          // amax = f * 2^x, f in [0.5, 1): e = x - 15; zeros (and inf/NaN) keep e = 0
-          const int e = (amax[j] > 0.f && amax[j] <= 3.402823466e38f) ? __builtin_amdgcn_frexp_expf(amax[j]) - 15 : 0;
-          if (r >= job.rows_here || n >= N) continue;
-          const long long row = job.row_begin + job.m0 + r;
-          char* dst = gemm_out_row<2>(p, row);
-          if (c8 == 0) p.c_exp[row * p.c_exp_blocks + job.n0 / kHBlock] = e;
-          if (n + 8 <= N) {
-            half8 o;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = static_cast<_Float16>(ldexpf(v[j][i], -e));
-            *reinterpret_cast<half8*>(dst + static_cast<long long>(n) * 2) = o;
-          } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-              if (n + i < N) reinterpret_cast<_Float16*>(dst)[n + i] = static_cast<_Float16>(ldexpf(v[j][i], -e));
-          }
-        }
-      }
-      return;
-    }
     for (int q = tid; q < BM * 32; q += THREADS) {
       const int r = q >> 5;
       const int c8 = (q & 31) * 8;
@@ -378,6 +409,76 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
           reinterpret_cast<uint16_t*>(dst)[n + i] = f32_to_bf16(src[i]);
       }
     }
+  } else if constexpr (YF16) {
+    // Scaled fp16 y, one exponent per row and 256 columns (waves 0-3 hold
+    // block 0 of the tile, waves 4-7 block 1).  The accumulators hold y
+    // transposed: lane l, element i -> output column 64 wave + 16 t +
+    // 4 (l / 16) + i, token row 16 m + l % 16, scaled by 2^-erow[row].
+    // The codes do not depend on erow: with amax the block's largest |acc|
+    // = f 2^x (f in [1/2, 1)), code = acc * 2^(15 - x) and the block
+    // exponent is x - 15 + erow (0 for a block of zeros).
+    float rm[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      float v = 0.f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaxf(v, fabsf(acc[m][t][i]));
+      rm[m] = v;
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) rm[m] = fmaxf(rm[m], __shfl_xor(rm[m], 16, 64));
+#pragma unroll
+    for (int m = 0; m < 8; ++m) rm[m] = fmaxf(rm[m], __shfl_xor(rm[m], 32, 64));
+    if (lgrp == 0) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) wmax[(m * 16 + lrow) * WAVES + wave] = rm[m];
+    }
+    __syncthreads();
+    // codes into LDS, rows of 512 fp16 at a 1040-byte stride (8-byte writes
+    // of the 64 lanes fall on distinct banks)
+    constexpr int CROW = LDC * 4;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int r = m * 16 + lrow;
+      const f32x4 q = *reinterpret_cast<const f32x4*>(wmax + r * WAVES + (wave & 4));
+      const float amax = fmaxf(fmaxf(q[0], q[1]), fmaxf(q[2], q[3]));
+      const bool scaled = amax > 0.f && amax <= 3.402823466e38f;
+      const int x = scaled ? __builtin_amdgcn_frexp_expf(amax) : 15;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        const h4 c = h4{static_cast<_Float16>(ldexpf(acc[m][t][0], 15 - x)),
+                        static_cast<_Float16>(ldexpf(acc[m][t][1], 15 - x)),
+                        static_cast<_Float16>(ldexpf(acc[m][t][2], 15 - x)),
+                        static_cast<_Float16>(ldexpf(acc[m][t][3], 15 - x))};
+        *reinterpret_cast<h4*>(smem + r * CROW + (wave * 64 + t * 16 + lgrp * 4) * 2) = c;
+      }
+      const int blk0 = job.n0 + (wave & 4) * 64;  // first column of this wave's block
+      if ((wave & 3) == 0 && lgrp == 0 && r < job.rows_here && blk0 < N)
+        p.c_exp[(job.row_begin + job.m0 + r) * static_cast<long long>(p.c_exp_blocks) + blk0 / kHBlock] =
+            scaled ? x - 15 + erow[r] : 0;
+    }
+    __syncthreads();
+    // rows out: a wave stores one row (512 columns, 1 KB) per instruction;
+    // y is read once, by the combine
+    static_assert(BM % WAVES == 0, "rows split evenly over the waves");
+#pragma unroll
+    for (int j = 0; j < BM / WAVES; ++j) {
+      const int r = wave * (BM / WAVES) + j;
+      if (r >= job.rows_here) break;
+      const int n = job.n0 + lane * 8;
+      const half8 v = *reinterpret_cast<const half8*>(smem + r * CROW + lane * 16);
+      _Float16* dst = reinterpret_cast<_Float16*>(gemm_out_row<2>(p, job.row_begin + job.m0 + r));
+      if (n + 8 <= N) {
+        __builtin_nontemporal_store(__builtin_bit_cast(f32x4, v), reinterpret_cast<f32x4*>(dst + n));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (n + i < N) dst[n + i] = v[i];
+      }
+    }
   } else {
     // fp32 output staged through LDS in two passes of 256 columns (waves 0-3,
     // then 4-7), so that each lane stores 16 bytes and a wave one contiguous
@@ -394,60 +495,6 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
               Cs[(m * 16 + lgrp * 4 + i) * LDC + (wave & 3) * 64 + t * 16 + lrow] = acc[m][t][i];
       }
       __syncthreads();
-      if constexpr (YF16) {
-        // scaled fp16 y: one wave holds a row's 256 columns of this pass, one
-        // exponent block; e puts the block's largest |y| * 2^-e in
-        // [2^14, 2^15) (0 for a block of zeros).  Rows go in batches of RB
-        // per wave so that their latency chains overlap.
-        constexpr int ITER = BM * 64 / THREADS, RB = 4;
-        static_assert(BM * 64 % THREADS == 0 && ITER % RB == 0, "every lane takes part in each row's reduction");
-        for (int it = 0; it < ITER; it += RB) {
-          f32x4 o[RB];
-          float amax[RB];
-#pragma unroll
-          for (int j = 0; j < RB; ++j) {
-            const int q = tid + (it + j) * THREADS;
-            const int r = q >> 6;
-            const int n = job.n0 + half * 256 + (q & 63) * 4;
-            const float* src = Cs + r * LDC + (q & 63) * 4;
-            const int ea = erow[r];
-            o[j] = f32x4{ldexpf(src[0], ea), ldexpf(src[1], ea), ldexpf(src[2], ea), ldexpf(src[3], ea)};
-            amax[j] = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (n + i < N) amax[j] = fmaxf(amax[j], fabsf(o[j][i]));
-          }
-#pragma unroll
-          for (int j = 0; j < RB; ++j) amax[j] = wave_fmax_nonneg(amax[j]);
-#pragma unroll
-          for (int j = 0; j < RB; ++j) {
-            const int q = tid + (it + j) * THREADS;
-            const int r = q >> 6;
-            const int c4 = (q & 63) * 4;
-            const int n = job.n0 + half * 256 + c4;
-            const int e =
-                (amax[j] > 0.f && amax[j] <= 3.402823466e38f) ? __builtin_amdgcn_frexp_expf(amax[j]) - 15 : 0;
-            if (r >= job.rows_here || n >= N) continue;
-            const long long row = job.row_begin + job.m0 + r;
-            _Float16* dst = reinterpret_cast<_Float16*>(gemm_out_row<2>(p, row));
-            if (c4 == 0) p.c_exp[row * p.c_exp_blocks + (job.n0 + half * 256) / kHBlock] = e;
-            if (n + 4 <= N) {
-              typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-              const h4 hv = h4{static_cast<_Float16>(ldexpf(o[j][0], -e)), static_cast<_Float16>(ldexpf(o[j][1], -e)),
-                               static_cast<_Float16>(ldexpf(o[j][2], -e)), static_cast<_Float16>(ldexpf(o[j][3], -e))};
-              // y is read once, by the combine
-              typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-              __builtin_nontemporal_store(__builtin_bit_cast(u32x2, hv), reinterpret_cast<u32x2*>(dst + n));
-            } else {
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (n + i < N) dst[n + i] = static_cast<_Float16>(ldexpf(o[j][i], -e));
-            }
-          }
-        }
-        __syncthreads();
-        continue;
-      }
       for (int q = tid; q < BM * 64; q += THREADS) {
         const int r = q >> 6;
         const int c4 = (q & 63) * 4;
@@ -478,6 +525,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_prefill_kernel(GemmLaunch p) 
   constexpr int BN = DUAL ? 256 : 512;  // output columns per block
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   __shared__ int erow[BM];
+  // scaled fp16 outputs: row maxima per wave
+  __shared__ __attribute__((aligned(16))) float wmax[(YF16 || (DUAL && F16)) ? BM * WAVES : 1];
   static_assert(U * A_SLOT + BM * kMaxHBlocks * 4 <= SMEM,
                 "A ring and block shifts inside the epilogue tile");
   static_assert(!DUAL || BN == kHBlock, "one exponent per gate/up tile row");
@@ -501,11 +550,11 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_prefill_kernel(GemmLaunch p) 
   const bool n_act = DUAL ? (!PARTN || job.n0 + wave * 32 < N) : job.n0 + wave * 64 < N;
   const int ms = n_act ? min(4, (job.rows_here + 31) >> 5) * 2 : 0;
   switch (ms) {
-    case 8: tile_body<DUAL, 8, F16, YF16>(p, job, smem, nk, kt0, erow); break;
-    case 6: tile_body<DUAL, 6, F16, YF16>(p, job, smem, nk, kt0, erow); break;
-    case 4: tile_body<DUAL, 4, F16, YF16>(p, job, smem, nk, kt0, erow); break;
-    case 2: tile_body<DUAL, 2, F16, YF16>(p, job, smem, nk, kt0, erow); break;
-    default: tile_body<DUAL, 0, F16, YF16>(p, job, smem, nk, kt0, erow); break;
+    case 8: tile_body<DUAL, 8, F16, YF16>(p, job, smem, nk, kt0, erow, wmax); break;
+    case 6: tile_body<DUAL, 6, F16, YF16>(p, job, smem, nk, kt0, erow, wmax); break;
+    case 4: tile_body<DUAL, 4, F16, YF16>(p, job, smem, nk, kt0, erow, wmax); break;
+    case 2: tile_body<DUAL, 2, F16, YF16>(p, job, smem, nk, kt0, erow, wmax); break;
+    default: tile_body<DUAL, 0, F16, YF16>(p, job, smem, nk, kt0, erow, wmax); break;
   }
 }
 
