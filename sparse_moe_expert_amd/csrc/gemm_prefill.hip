@@ -56,6 +56,11 @@ constexpr int A_SLOT = BM * SLICE_B;    // 8 KB of token rows per slice
 constexpr int U = 3;                    // ring slots: A staging, A in LDS, weights (U - 1 ahead)
 constexpr int LDC = 256 + 4;            // fp32 epilogue tile row stride
 constexpr int SMEM = BM * LDC * 4;      // epilogue tile; the A ring (24 KB) fits inside
+// One block per CU: chunks of 32 consecutive tiles, one per CU of an XCD,
+// are dealt round-robin to the XCDs (measured at T=16384: with contiguous
+// runs per XCD, the XCD holding the shared expert's tiles ended 7% after
+// the others)
+constexpr int kXcdChunk = 32;
 
 // 16-byte load through a global (address space 1) pointer: a generic pointer
 // read from the group table would compile to a flat load, which the
@@ -532,7 +537,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_prefill_kernel(GemmLaunch p) 
   static_assert(!DUAL || BN == kHBlock, "one exponent per gate/up tile row");
 
   TileJob job;
-  if (!find_tile<BM, BN, DUAL>(p, job)) return;
+  if (!find_tile<BM, BN, DUAL, kXcdChunk>(p, job)) return;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int nk = p.K / KE;
@@ -569,7 +574,8 @@ hipError_t launch_prefill(const GemmLaunch& g, hipStream_t st) {
       g.single_group_rows > 0 ? (g.single_group_rows + BM - 1) / BM : g.grid_mtiles_upper;
   const long long total = ub_m * ntn;
   if (total <= 0) return hipSuccess;
-  const long long grid = ((total + 7) / 8) * 8;
+  const long long c8 = 8LL * xcd_chunk<kXcdChunk>(total);
+  const long long grid = ((total + c8 - 1) / c8) * c8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 gd(static_cast<unsigned>(grid), static_cast<unsigned>(splits));
   // scaled fp16: gate/up writes h that way (c_exp); the projection reads A

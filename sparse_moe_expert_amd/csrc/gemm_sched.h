@@ -18,22 +18,41 @@ struct TileJob {
 };
 
 // Blocks are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8).
-// Remap so that XCD x owns the contiguous run [x * per, (x + 1) * per) of
-// the tile list: consecutive tiles then share that XCD's L2.  Returns false
-// if the block has no tile.  Tiles run group by group; inside a group n-tile
-// major, m-tile minor.
+// Remap so that consecutive tiles run on one XCD and share its L2:
+//  * CHUNK = 0: XCD x owns the contiguous run [x * per, (x + 1) * per) of
+//    the tile list (grid: a multiple of 8);
+//  * CHUNK > 0: the list is cut into chunks of c tiles dealt round-robin to
+//    the XCDs (chunk j to XCD j % 8), so that the work of every part of the
+//    list -- the shared experts' full tiles at its end, say -- is spread over
+//    all XCDs; c = xcd_chunk<CHUNK>(upper bound on the tiles), at most CHUNK
+//    and small enough that every XCD gets a chunk (grid: a multiple of 8 c).
+// Returns false if the block has no tile.  Tiles run group by group; inside
+// a group n-tile major, m-tile minor.
 // `b` is the block index (blockIdx.x, or a virtual block of a persistent
 // grid whose size is a multiple of 8, which keeps b % 8 the XCD).
-template <int BM, int BN, bool DUAL>
+template <int CHUNK>
+__host__ __device__ inline int xcd_chunk(long long tiles_upper) {
+  return static_cast<int>(tiles_upper < 8LL * CHUNK ? (tiles_upper + 7) / 8 : CHUNK);
+}
+
+template <int BM, int BN, bool DUAL, int CHUNK = 0>
 __device__ __forceinline__ bool find_tile_at(const GemmLaunch& p, TileJob& job, int b) {
   const int ntn = (p.N + BN - 1) / BN;
   const int total_m =
       p.single_group_rows > 0 ? (p.single_group_rows + BM - 1) / BM : *p.total_mtiles;
   const int total = total_m * ntn;
-  const int per_xcd = (total + 7) >> 3;
   const int slot = b >> 3;
-  if (slot >= per_xcd) return false;
-  const int w_id = (b & 7) * per_xcd + slot;
+  int w_id;
+  if constexpr (CHUNK > 0) {
+    const long long ub_m =
+        p.single_group_rows > 0 ? (p.single_group_rows + BM - 1) / BM : p.grid_mtiles_upper;
+    const int c = max(xcd_chunk<CHUNK>(ub_m * ntn), 1);
+    w_id = ((slot / c) * 8 + (b & 7)) * c + slot % c;
+  } else {
+    const int per_xcd = (total + 7) >> 3;
+    if (slot >= per_xcd) return false;
+    w_id = (b & 7) * per_xcd + slot;
+  }
   if (w_id >= total) return false;
   int mt = w_id / ntn;
   int nt = w_id - mt * ntn;
@@ -76,9 +95,9 @@ __device__ __forceinline__ bool find_tile_at(const GemmLaunch& p, TileJob& job, 
   return true;
 }
 
-template <int BM, int BN, bool DUAL>
+template <int BM, int BN, bool DUAL, int CHUNK = 0>
 __device__ __forceinline__ bool find_tile(const GemmLaunch& p, TileJob& job) {
-  return find_tile_at<BM, BN, DUAL>(p, job, blockIdx.x);
+  return find_tile_at<BM, BN, DUAL, CHUNK>(p, job, blockIdx.x);
 }
 
 __device__ __forceinline__ int gemm_a_source_row(const GemmLaunch& p, int row) {
