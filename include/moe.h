@@ -133,15 +133,17 @@ typedef struct moe_weights {
  * [rows, cols] matrices of `dtype` elements from src into dst in the
  * MOE_LAYOUT_TILED order.  Each matrix is cut into 16-row x 64-byte tiles
  * (1 KB); tiles are stored row group by row group, and along the row inside
- * a row group; inside a tile each of its 16 rows keeps its 64 bytes
- * contiguous.  So byte b of row r of matrix m lands at
- *   m*rows*rb + (r/16)*16*rb + (b/64)*1024 + (r%16)*64 + b%64,
+ * a row group; inside a tile the 16-byte chunks are stored chunk-major
+ * (chunk c of the tile's 16 rows, then chunk c + 1).  So byte b of row r of
+ * matrix m lands at
+ *   m*rows*rb + (r/16)*16*rb + (b/64)*1024 + ((b%64)/16)*256 + (r%16)*16 + b%16,
  * rb = cols * element size.  Matrix m starts at the same byte offset in
  * both layouts, so per-expert pointers and the FP8 block scales are
  * unchanged.  Use: pack w_gate_up with (E, 2I, H), w_down with (E, H, I),
  * and the shared ones with S, then set expert_layout = MOE_LAYOUT_TILED.
  * Every GEMM load instruction (64 lanes x 16 bytes) then reads one whole
- * tile, 1 KB contiguous, instead of 16 pieces one weight row apart.
+ * tile, 1 KB contiguous with lane l at byte 16 l, instead of 16 pieces one
+ * weight row apart.
  * src and dst: device, 16-byte aligned, not overlapping, count*rows*rb
  * bytes each.  count >= 0 (0: no-op), rows > 0, cols > 0 and dtype a
  * moe_dtype_t, else MOE_ERR_INVALID_ARG (also for null, misaligned or

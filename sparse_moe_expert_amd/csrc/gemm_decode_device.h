@@ -61,7 +61,7 @@ __device__ __forceinline__ void decode_tile(const GemmLaunch& p, int b) {
     } else {
       wr = min(wn0 + t * 16 + lrow, N - 1);
     }
-    bptr[t] = job.W + w_tile_row_off(p.w_tiled, wr, rowb_b) + lgrp * 16;
+    bptr[t] = job.W + w_tile_row_off(p.w_tiled, wr, rowb_b) + w_tile_k_off(p.w_tiled, lgrp * 16);
   }
   const char* aptr[NA][MT];
 #pragma unroll

@@ -49,6 +49,7 @@ constexpr int A_DMA = A_SLOT / 16 / THREADS;  // 16-byte DMA chunks per thread p
 constexpr int W_LOADS = 4;                  // 16-byte weight loads per thread per step
 constexpr int OPS = A_DMA + W_LOADS;        // vector memory ops per thread per step
 constexpr int MAX_KB = 64;                  // K <= 8192
+constexpr int kXcdChunk = 32;               // tiles per XCD chunk: one block per CU, 32 CUs per XCD
 constexpr int SA_OFF = S * A_SLOT;          // token scales [kb][row] fp32
 constexpr int SB_OFF = SA_OFF + MAX_KB * BM * 4;  // weight block scales [2][kb] fp32
 constexpr int LDC = 128 + 4;                // fp32 epilogue tile row stride
@@ -122,7 +123,7 @@ __device__ __forceinline__ void tile_body(const GemmLaunch& p, const TileJob& jo
     } else {
       row = min(job.n0 + wave * 32 + t * 16 + (lane & 15), N - 1);
     }
-    w_src[t] = job.W + w_tile_row_off(p.w_tiled, row, rowb_b) + 16 * (lane >> 4);
+    w_src[t] = job.W + w_tile_row_off(p.w_tiled, row, rowb_b) + w_tile_k_off(p.w_tiled, 16 * (lane >> 4));
   }
   // the block's two weight row blocks (DUAL: gate, up; projection: rows
   // [n0, n0 + 128) and [n0 + 128, n0 + 256)) stage their scales in LDS
@@ -343,7 +344,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_fp8s_kernel(GemmLaunch p) {
   constexpr int BN = DUAL ? 128 : 256;  // output columns per block
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   TileJob job;
-  if (!find_tile<BM, BN, DUAL>(p, job)) return;
+  if (!find_tile<BM, BN, DUAL, kXcdChunk>(p, job)) return;
   const int mt = (job.rows_here + 63) / 64 * 4;  // token tiles, a multiple of 4
   if (mt <= 4) tile_body<DUAL, 4>(p, job, smem);
   else if (mt <= 8) tile_body<DUAL, 8>(p, job, smem);
@@ -360,7 +361,8 @@ hipError_t launch_fp8s(const GemmLaunch& g, hipStream_t st) {
       g.single_group_rows > 0 ? (g.single_group_rows + BM - 1) / BM : g.grid_mtiles_upper;
   const long long total = ub_m * ntn;
   if (total <= 0) return hipSuccess;
-  const long long grid = ((total + 7) / 8) * 8;
+  const long long c8 = 8LL * xcd_chunk<kXcdChunk>(total);
+  const long long grid = ((total + c8 - 1) / c8) * c8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_fp8s_kernel<DUAL>), dim3(static_cast<unsigned>(grid)), dim3(THREADS), 0,
                      st, g);

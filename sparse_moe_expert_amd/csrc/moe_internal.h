@@ -86,20 +86,24 @@ inline size_t kind_size(int kind) { return kind == K_F32 ? 4 : kind == K_BF16 ? 
 // Tiled weight storage: a row-major [rows, K] matrix (rows a multiple of 16,
 // K * element size a multiple of 64 bytes) cut into 16-row x 64-byte tiles
 // of 1 KB.  Tiles are stored row group by row group, and along K inside a
-// row group; inside a tile each row's 64 bytes are contiguous.  One GEMM
-// load instruction of 64 lanes x 16 bytes then reads one tile, 1 KB
-// contiguous.  The byte offset of (row, byte b of the row) splits into a row
-// part and a K part, which the kernels add separately; for K offsets that
-// are multiples of 64 the K part is additive (w_tile_k_off(a + b) =
+// row group.  Inside a tile the 16-byte chunks go chunk-major: chunk c (bytes
+// [16 c, 16 c + 16) of the tile's 64) of tile row r sits at 256 c + 16 r.
+// The MFMA operand fragment of a 16-row tile and 64-byte K step gives lane l
+// row l % 16 and chunk l / 16, so one load instruction of 64 lanes x 16 bytes
+// reads the whole tile with lane l at byte 16 l: 1 KB contiguous, in lane
+// order.  The byte offset of (row, byte b of the row) splits into a row part
+// and a K part, which the kernels add separately; for K offsets that are
+// multiples of 64 the K part is additive (w_tile_k_off(a + b) =
 // w_tile_k_off(a) + w_tile_k_off(b) when a % 64 == 0).
 constexpr int kTileRows = 16;
 constexpr int kTileBytes = 64;
 __host__ __device__ inline long long w_tile_row_off(int tiled, int row, long long row_bytes) {
-  return tiled ? static_cast<long long>(row >> 4) * (row_bytes * kTileRows) + (row & 15) * kTileBytes
+  return tiled ? static_cast<long long>(row >> 4) * (row_bytes * kTileRows) + (row & 15) * 16
                : static_cast<long long>(row) * row_bytes;
 }
 __host__ __device__ inline long long w_tile_k_off(int tiled, long long kbyte) {
-  return tiled ? (kbyte >> 6) * (kTileRows * kTileBytes) + (kbyte & 63) : kbyte;
+  return tiled ? (kbyte >> 6) * (kTileRows * kTileBytes) + ((kbyte & 63) >> 4) * (kTileRows * 16) + (kbyte & 15)
+               : kbyte;
 }
 
 // ---------------------------------------------------------------- launchers

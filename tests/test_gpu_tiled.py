@@ -35,12 +35,13 @@ def _need_gpu():
 
 def tiled_bytes(a: np.ndarray) -> np.ndarray:
     """[n, rows, cols] row-major -> the bytes of the tiled order: 16-row x
-    64-byte tiles, row group major, then along the row; rows of a tile
-    contiguous inside it."""
+    64-byte tiles, row group major, then along the row; inside a tile the
+    16-byte chunks chunk-major (chunk c of tile row r at 256 c + 16 r)."""
     n, rows = a.shape[:2]
     b = np.ascontiguousarray(a).view(np.uint8).reshape(n, rows, -1)
     rb = b.shape[2]
-    t = b.reshape(n, rows // 16, 16, rb // 64, 64).transpose(0, 1, 3, 2, 4)
+    # axes: matrix, row group, tile row, tile column, chunk, byte
+    t = b.reshape(n, rows // 16, 16, rb // 64, 4, 16).transpose(0, 1, 3, 4, 2, 5)
     return np.ascontiguousarray(t).reshape(-1)
 
 
