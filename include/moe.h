@@ -114,7 +114,19 @@ typedef struct moe_config {
  *               128 x 128 block of the matching weight, i.e. s_gate_up
  *               [E, 2I/128, H/128], s_down [E, H/128, I/128], and the same
  *               with S for the shared ones.  Dequantised weight =
- *               e4m3 code * block scale.                                   */
+ *               e4m3 code * block scale.
+ *  w_down_f16, w_sh_down_f16: optional (NULL: not used), bf16 experts only:
+ *               fp16 copies of w_down and w_sh_down in the same layout, made
+ *               once with moe_convert_bf16_to_f16.  Where h between the two
+ *               GEMMs is scaled fp16 (the large-tile path, about 96 or more
+ *               rows per expert), the down GEMM multiplies fp16 h by fp16
+ *               weights and otherwise converts every bf16 weight fragment in
+ *               registers, once per 128-row tile that reads it; with the
+ *               copies it reads them instead.  Same conversion, so the same
+ *               output bit for bit.  w_sh_down_f16 is required with
+ *               w_down_f16 when S > 0; either without w_down_f16, or with
+ *               non-bf16 experts: MOE_ERR_INVALID_ARG.  Other paths ignore
+ *               them.                                                      */
 typedef struct moe_weights {
   const void* w_router;
   const float* router_bias;
@@ -126,6 +138,8 @@ typedef struct moe_weights {
   const void* w_sh_down;
   const float* s_sh_gate_up;
   const float* s_sh_down;
+  const void* w_down_f16;
+  const void* w_sh_down_f16;
 } moe_weights_t;
 
 /* Expert weight storage [D1 «并行策略字段»: gate_up_proj and down_proj as
@@ -152,6 +166,18 @@ typedef struct moe_weights {
  * stream reaches that point. */
 moe_status_t moe_pack_expert_weights(const void* src, void* dst, int64_t count, int32_t rows,
                                      int32_t cols, int32_t dtype, moe_stream_t stream);
+
+/* Optional fp16 copy of bf16 down weights (moe_weights_t w_down_f16 and
+ * w_sh_down_f16).  No page fixes the arithmetic of the expert GEMMs beyond
+ * their bf16 weights; this is the conversion the large-tile down GEMM applies
+ * to each bf16 weight fragment, moved to load time: each of the n bf16 values
+ * of src becomes the fp16 value rounded toward zero (exact for |w| in
+ * [2^-14, 65504]; below that the fp16 subnormal toward zero; beyond it
+ * +-65504; inf and NaN kept).  Element order is kept, so a tiled src gives
+ * a tiled dst.  src and dst: device, 16-byte aligned, n*2 bytes each, not
+ * overlapping; n >= 0 (0: no-op) and a multiple of 8, else
+ * MOE_ERR_INVALID_ARG.  Enqueued on `stream`. */
+moe_status_t moe_convert_bf16_to_f16(const void* src, void* dst, int64_t n, moe_stream_t stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* moe_status_string(moe_status_t status);

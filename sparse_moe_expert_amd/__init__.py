@@ -23,6 +23,7 @@ _BINDING = (
     "MOE_WS_COUNTS", "MOE_WS_OFFSETS", "MOE_WS_PERM", "MOE_WS_INV", "MOE_WS_H",
     "MOE_WS_H_SCALES", "MOE_WS_H_LO", "MOE_WS_Y", "MOE_WS_Y_SHARED", "MOE_WS_H_EXP", "MOE_WS_BARRIER", "MOE_WS_Y_EXP",
     "moe_layer_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "moe_stream_read", "moe_fused_set_spin_limit",
+    "moe_convert_bf16_to_f16",
 )
 
 __all__ = list(_BINDING)

@@ -30,7 +30,7 @@ EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_version", "moe_wor
            "moe_combine", "moe_quantize_fp8", "moe_layer_forward", "moe_layer_forward_timed",
            "moe_rmsnorm", "moe_block_forward", "moe_layer_forward_fused",
            "moe_pack_expert_weights", "moe_layer_forward_noalloc", "moe_stream_read",
-           "moe_fused_set_spin_limit")
+           "moe_fused_set_spin_limit", "moe_convert_bf16_to_f16")
 
 
 class MoEError(RuntimeError):
@@ -53,7 +53,7 @@ class moe_config_t(ctypes.Structure):
 class moe_weights_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w_router", "router_bias", "w_gate_up", "w_down", "s_gate_up", "s_down",
-        "w_sh_gate_up", "w_sh_down", "s_sh_gate_up", "s_sh_down")]
+        "w_sh_gate_up", "w_sh_down", "s_sh_gate_up", "s_sh_down", "w_down_f16", "w_sh_down_f16")]
 
 
 def _load():
@@ -84,6 +84,7 @@ def _load():
         "moe_quantize_fp8": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32, P, P, P]),
         "moe_pack_expert_weights": (ctypes.c_int, [P, P, ctypes.c_int64, ctypes.c_int32,
                                                    ctypes.c_int32, ctypes.c_int32, P]),
+        "moe_convert_bf16_to_f16": (ctypes.c_int, [P, P, ctypes.c_int64, P]),
         "moe_layer_forward": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P, SZ, P]),
         "moe_layer_forward_timed": (ctypes.c_int, [CP, WP, P, P, I32P, I32P, P, SZ, P,
                                                    ctypes.POINTER(ctypes.c_void_p)]),
@@ -145,10 +146,10 @@ def _stream(stream) -> int | None:
 
 def make_weights(w_router=None, router_bias=None, w_gate_up=None, w_down=None, s_gate_up=None,
                  s_down=None, w_sh_gate_up=None, w_sh_down=None, s_sh_gate_up=None,
-                 s_sh_down=None) -> moe_weights_t:
+                 s_sh_down=None, w_down_f16=None, w_sh_down_f16=None) -> moe_weights_t:
     return moe_weights_t(*(_ptr(t) for t in (w_router, router_bias, w_gate_up, w_down, s_gate_up,
                                              s_down, w_sh_gate_up, w_sh_down, s_sh_gate_up,
-                                             s_sh_down)))
+                                             s_sh_down, w_down_f16, w_sh_down_f16)))
 
 
 def _check(status: int, where: str):
@@ -219,6 +220,13 @@ def moe_pack_expert_weights(src, dst, count, rows, cols, dtype, stream=None):
     dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
     _check(LIB.moe_pack_expert_weights(_ptr(src), _ptr(dst), int(count), int(rows), int(cols), dt,
                                        _stream(stream)), "moe_pack_expert_weights")
+
+
+def moe_convert_bf16_to_f16(src, dst, n, stream=None):
+    """n bf16 values of src -> fp16 in dst, rounded toward zero (the fp16
+    copy of bf16 down weights, moe_weights_t w_down_f16 / w_sh_down_f16)."""
+    _check(LIB.moe_convert_bf16_to_f16(_ptr(src), _ptr(dst), int(n), _stream(stream)),
+           "moe_convert_bf16_to_f16")
 
 
 def moe_layer_forward(cfg, weights, x, out, opt_counts=None, opt_tie_counts=None, workspace=None,

@@ -488,7 +488,7 @@ hipError_t launch_gemm(int a_kind, int out_kind, TileShape ts, const GemmLaunch&
     if (g.A_lo || g.C_lo) return hipErrorInvalidValue;  // one-term h only
     return launch_gemm_prefill(dual, g, st);
   }
-  if (g.c_exp || g.a_exp) return hipErrorInvalidValue;  // scaled fp16 h: large-tile kernel only
+  if (g.c_exp || g.a_exp || g.w16) return hipErrorInvalidValue;  // scaled fp16 h: large-tile kernel only
   if (gemm_fp8s_supported(a_kind, out_kind, ts, dual)) {
     if (g.A_lo || g.C_lo) return hipErrorInvalidValue;
     return launch_gemm_fp8s(dual, g, st);

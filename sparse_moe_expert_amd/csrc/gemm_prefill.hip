@@ -122,7 +122,9 @@ __device__ __forceinline__ half8 bf16x8_to_f16(const bf16x8& w) {
 // row by 2^e in its epilogue.  erow: BM ints of LDS outside smem.
 // YF16 (projection of fp16 h): y leaves as fp16 codes with exponents per row
 // and 256 columns (c_exp); wmax: BM x WAVES floats of LDS for the row maxima.
-template <bool DUAL, int MS, bool F16, bool YF16>
+// W16 (projection of fp16 h): the weights are already fp16 (an fp16 copy
+// made at load time by the same conversion), so no per-fragment conversion.
+template <bool DUAL, int MS, bool F16, bool YF16, bool W16>
 __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, char* smem, int nk,
                                           int kt0, int* erow, float* wmax) {
   const int tid = threadIdx.x;
@@ -272,7 +274,7 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
         af[m] = *reinterpret_cast<const half8*>(As + swz(m * 16 + (lane & 15), lane >> 4));
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const half8 bf = bf16x8_to_f16(b_ring[R][t]);
+        const half8 bf = W16 ? __builtin_bit_cast(half8, b_ring[R][t]) : bf16x8_to_f16(b_ring[R][t]);
 #pragma unroll
         for (int m = 0; m < MS; ++m)
           acc[m][t] = TRN ? __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, af[m], acc[m][t], 0, 0, 0)
@@ -285,7 +287,7 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
       __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU
+        if constexpr (!W16) __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -525,7 +527,7 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
   }
 }
 
-template <bool DUAL, bool PARTN, bool F16, bool YF16>
+template <bool DUAL, bool PARTN, bool F16, bool YF16, bool W16 = false>
 __global__ __launch_bounds__(THREADS, 1) void gemm_prefill_kernel(GemmLaunch p) {
   constexpr int BN = DUAL ? 256 : 512;  // output columns per block
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
@@ -538,6 +540,9 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_prefill_kernel(GemmLaunch p) 
 
   TileJob job;
   if (!find_tile<BM, BN, DUAL, kXcdChunk>(p, job)) return;
+  if constexpr (W16)  // the group's matrix in the fp16 copy (same layout and size)
+    job.W = reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(job.W) +
+                                          (job.row_begin >= p.R ? p.w16_delta_sh : p.w16_delta));
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int nk = p.K / KE;
@@ -555,11 +560,11 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_prefill_kernel(GemmLaunch p) 
   const bool n_act = DUAL ? (!PARTN || job.n0 + wave * 32 < N) : job.n0 + wave * 64 < N;
   const int ms = n_act ? min(4, (job.rows_here + 31) >> 5) * 2 : 0;
   switch (ms) {
-    case 8: tile_body<DUAL, 8, F16, YF16>(p, job, smem, nk, kt0, erow, wmax); break;
-    case 6: tile_body<DUAL, 6, F16, YF16>(p, job, smem, nk, kt0, erow, wmax); break;
-    case 4: tile_body<DUAL, 4, F16, YF16>(p, job, smem, nk, kt0, erow, wmax); break;
-    case 2: tile_body<DUAL, 2, F16, YF16>(p, job, smem, nk, kt0, erow, wmax); break;
-    default: tile_body<DUAL, 0, F16, YF16>(p, job, smem, nk, kt0, erow, wmax); break;
+    case 8: tile_body<DUAL, 8, F16, YF16, W16>(p, job, smem, nk, kt0, erow, wmax); break;
+    case 6: tile_body<DUAL, 6, F16, YF16, W16>(p, job, smem, nk, kt0, erow, wmax); break;
+    case 4: tile_body<DUAL, 4, F16, YF16, W16>(p, job, smem, nk, kt0, erow, wmax); break;
+    case 2: tile_body<DUAL, 2, F16, YF16, W16>(p, job, smem, nk, kt0, erow, wmax); break;
+    default: tile_body<DUAL, 0, F16, YF16, W16>(p, job, smem, nk, kt0, erow, wmax); break;
   }
 }
 
@@ -587,6 +592,17 @@ hipError_t launch_prefill(const GemmLaunch& g, hipStream_t st) {
     return hipErrorInvalidValue;
   if (g.c_exp && g.c_exp_blocks != (g.N + kHBlock - 1) / kHBlock) return hipErrorInvalidValue;
   if (yf16 && !f16) return hipErrorInvalidValue;  // fp16 y only from fp16 h
+  const bool w16 = !DUAL && g.w16;
+  if ((g.w16 && DUAL) || (w16 && !f16)) return hipErrorInvalidValue;  // fp16 weights meet fp16 h only
+  if constexpr (!DUAL) {
+    if (w16) {
+      if (yf16)
+        hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, false, true, true, true>), gd, dim3(THREADS), 0, st, g);
+      else
+        hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, false, true, false, true>), gd, dim3(THREADS), 0, st, g);
+      return hipGetLastError();
+    }
+  }
   if (DUAL && g.N % BN != 0) {
     if (f16)
       hipLaunchKernelGGL((gemm_prefill_kernel<DUAL, true, true, false>), gd, dim3(THREADS), 0, st, g);

@@ -102,6 +102,12 @@ moe_status_t check_weights(const moe_config_t& c, const moe_weights_t* w, bool r
       if (!w->s_gate_up || !w->s_down) return MOE_ERR_INVALID_ARG;
       if (c.S > 0 && (!w->s_sh_gate_up || !w->s_sh_down)) return MOE_ERR_INVALID_ARG;
     }
+    // optional fp16 copies of the bf16 down weights
+    if (w->w_down_f16 || w->w_sh_down_f16) {
+      if (c.expert_dtype != MOE_BF16 || !w->w_down_f16 || !aligned16(w->w_down_f16))
+        return MOE_ERR_INVALID_ARG;
+      if (c.S > 0 && (!w->w_sh_down_f16 || !aligned16(w->w_sh_down_f16))) return MOE_ERR_INVALID_ARG;
+    }
   }
   return MOE_OK;
 }
@@ -227,7 +233,7 @@ hipError_t run_gate_up(const moe_config_t& c, const Layout& L, const void* x, co
 }
 
 hipError_t run_down(const moe_config_t& c, const Layout& L, void* y_sorted, void* y_shared,
-                    void* ws, hipStream_t st, bool y_f16 = false);
+                    void* ws, hipStream_t st, bool y_f16 = false, const moe_weights_t* w16 = nullptr);
 
 hipError_t record(void* const* events, int i, hipStream_t st) {
   if (!events) return hipSuccess;
@@ -283,7 +289,7 @@ hipError_t layer_run(const moe_config_t& c, const moe_weights_t* w, const void* 
   if (e == hipSuccess) e = run_gate_up_gemm(c, L, x, perm, ws, st);
   if (e == hipSuccess) e = record(events, 4, st);
   // inside the layer y stays in the workspace: scaled fp16 on the large-tile path
-  if (e == hipSuccess) e = run_down(c, L, y, ysh, ws, st, L.h_f16);
+  if (e == hipSuccess) e = run_down(c, L, y, ysh, ws, st, L.h_f16, w);
   if (e == hipSuccess) e = record(events, 5, st);
   if (e == hipSuccess)
     e = launch_combine(act_kind(c), y, ysh, L.h_f16 ? at<int32_t>(ws, L.yexp) : nullptr, tw, inv,
@@ -303,9 +309,10 @@ moe_status_t layer_impl(const moe_config_t* cfg, const moe_weights_t* w, const v
 }
 
 // y_f16 (the layer's own y, large-tile path): y and y_sh as scaled fp16 with
-// exponents in the workspace (yexp); otherwise fp32 into the given buffers
+// exponents in the workspace (yexp); otherwise fp32 into the given buffers.
+// w16: weights whose optional fp16 down copies the large-tile path reads.
 GemmLaunch down_launch(const moe_config_t& c, const Layout& L, void* y_sorted, void* y_shared,
-                       void* ws, bool y_f16 = false) {
+                       void* ws, bool y_f16 = false, const moe_weights_t* w16 = nullptr) {
   const bool fp8 = is_fp8(c);
   GemmLaunch g{};
   g.groups = at<GroupDesc>(ws, L.groups);
@@ -333,13 +340,24 @@ GemmLaunch down_launch(const moe_config_t& c, const Layout& L, void* y_sorted, v
   g.c_exp = (y_f16 && L.h_f16) ? at<int32_t>(ws, L.yexp) : nullptr;
   g.c_exp_blocks = (c.H + kHBlock - 1) / kHBlock;
   g.w_tiled = c.expert_layout == MOE_LAYOUT_TILED;
+  if (w16 && w16->w_down_f16 && L.h_f16) {
+    // the copies have the layout and size of w_down / w_sh_down (checked
+    // with the weights), so each group's fp16 matrix is its bf16 address
+    // plus the difference of the bases
+    g.w16 = 1;
+    g.w16_delta = static_cast<long long>(reinterpret_cast<uintptr_t>(w16->w_down_f16) -
+                                         reinterpret_cast<uintptr_t>(w16->w_down));
+    g.w16_delta_sh = c.S > 0 ? static_cast<long long>(reinterpret_cast<uintptr_t>(w16->w_sh_down_f16) -
+                                                      reinterpret_cast<uintptr_t>(w16->w_sh_down))
+                             : 0;
+  }
   return g;
 }
 
 hipError_t run_down(const moe_config_t& c, const Layout& L, void* y_sorted, void* y_shared,
-                    void* ws, hipStream_t st, bool y_f16) {
-  return launch_gemm(expert_kind(c), K_F32, L.dn, down_launch(c, L, y_sorted, y_shared, ws, y_f16),
-                     st);
+                    void* ws, hipStream_t st, bool y_f16, const moe_weights_t* w16) {
+  return launch_gemm(expert_kind(c), K_F32, L.dn,
+                     down_launch(c, L, y_sorted, y_shared, ws, y_f16, w16), st);
 }
 
 // Device address of `scratch` on the current device, looked up once per
@@ -669,6 +687,17 @@ moe_status_t moe_pack_expert_weights(const void* src, void* dst, int64_t count, 
     return MOE_ERR_INVALID_ARG;  // overlapping
   clear_stale_error();
   return hip_status(launch_pack_tiles(src, dst, count, rows, rb, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_convert_bf16_to_f16(const void* src, void* dst, int64_t n, moe_stream_t stream) {
+  if (n < 0 || n % 8 != 0 || n > LLONG_MAX / 2) return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return MOE_ERR_INVALID_ARG;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t bytes = static_cast<uintptr_t>(n) * 2;
+  if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;  // overlapping
+  clear_stale_error();
+  return hip_status(launch_convert_bf16_f16(src, dst, n, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,

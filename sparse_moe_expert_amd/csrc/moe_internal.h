@@ -159,10 +159,21 @@ struct GemmLaunch {
   // expert weights (groups' w_gu / w_dn) stored as 16-row x 64-byte tiles
   // (w_tile_row_off / w_tile_k_off); the router's b_single is always row-major
   int w_tiled;
+  // fp16 copy of the down weights (large-tile down GEMM of scaled fp16 h
+  // only; 0 = convert the bf16 fragments in registers).  The copy has w_dn's
+  // layout and size, so a group's fp16 matrix lies at its bf16 address plus
+  // the difference of the two bases: w16_delta for routed groups, and
+  // w16_delta_sh for shared ones (rows >= R).
+  int w16;
+  long long w16_delta;
+  long long w16_delta_sh;
 };
 
 hipError_t launch_gemm(int a_kind, int out_kind, TileShape ts, const GemmLaunch& g,
                        hipStream_t st);
+// n bf16 values -> fp16, rounded toward zero (moe_convert_bf16_to_f16);
+// n a multiple of 8, 16-byte aligned buffers.
+hipError_t launch_convert_bf16_f16(const void* src, void* dst, long long n, hipStream_t st);
 // Large-tile bf16 kernel (gemm_prefill.hip): 128 rows x 256 h-columns
 // (gate/up) or 128 rows x 512 output columns (projection), bf16 operands.
 bool gemm_prefill_supported(int a_kind, int out_kind, TileShape ts, bool dual);

@@ -38,7 +38,35 @@ __global__ __launch_bounds__(256) void pack_tiles_kernel(const uint4* __restrict
   }
 }
 
+// Eight bf16 values -> eight fp16 per thread: each pair of bf16 widened to
+// fp32 (exact) and packed to fp16 rounded toward zero, the instruction the
+// large-tile down GEMM uses on its weight fragments.
+__global__ __launch_bounds__(256) void convert_bf16_f16_kernel(const uint4* __restrict__ src,
+                                                               uint4* __restrict__ dst,
+                                                               long long chunks) {
+  for (long long q = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; q < chunks;
+       q += static_cast<long long>(gridDim.x) * blockDim.x) {
+    const uint4 v = src[q];
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[i] << 16),
+                                                                     __uint_as_float(w[i] & 0xffff0000u)));
+    dst[q] = uint4{w[0], w[1], w[2], w[3]};
+  }
+}
+
 }  // namespace
+
+hipError_t launch_convert_bf16_f16(const void* src, void* dst, long long n, hipStream_t st) {
+  const long long chunks = n / 8;
+  if (chunks <= 0) return hipSuccess;
+  const long long want = (chunks + 255) / 256;
+  const unsigned grid = static_cast<unsigned>(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(convert_bf16_f16_kernel, dim3(grid), dim3(256), 0, st,
+                     static_cast<const uint4*>(src), static_cast<uint4*>(dst), chunks);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_tiles(const void* src, void* dst, long long count, int rows,
                              long long row_bytes, hipStream_t st) {

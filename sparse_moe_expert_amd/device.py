@@ -54,9 +54,12 @@ class DeviceLayer:
 
     tiled=True stores the expert weights in MOE_LAYOUT_TILED order: they are
     uploaded row-major, packed on the device once, and the row-major copies
-    are dropped."""
+    are dropped.  down_f16=True (bf16 experts) also keeps the fp16 copies of
+    the down weights (moe_convert_bf16_to_f16) that the large-tile down GEMM
+    reads instead of converting bf16 fragments itself."""
 
-    def __init__(self, cfg, inp: dict, device: str = "cuda", tiled: bool = False):
+    def __init__(self, cfg, inp: dict, device: str = "cuda", tiled: bool = False,
+                 down_f16: bool = False):
         self.cfg = cfg
         self.device = device
         self.tiled = tiled
@@ -80,12 +83,18 @@ class DeviceLayer:
         if tiled:
             for key in ("w_gate_up", "w_down", "w_sh_gate_up", "w_sh_down"):
                 t[key] = pack_expert_weights(t[key], ek)
+        if down_f16:
+            for key in ("w_down", "w_sh_down"):
+                if t[key].numel():
+                    t[key + "_f16"] = torch.empty(t[key].shape, dtype=torch.float16, device=device)
+                    _lib.moe_convert_bf16_to_f16(t[key], t[key + "_f16"], t[key].numel())
         self.t = t
         self.weights = make_weights(
             w_router=t["w_router"], router_bias=t["bias"], w_gate_up=t["w_gate_up"],
             w_down=t["w_down"], s_gate_up=t.get("s_gate_up"), s_down=t.get("s_down"),
             w_sh_gate_up=t["w_sh_gate_up"], w_sh_down=t["w_sh_down"],
-            s_sh_gate_up=t.get("s_sh_gate_up"), s_sh_down=t.get("s_sh_down"))
+            s_sh_gate_up=t.get("s_sh_gate_up"), s_sh_down=t.get("s_sh_down"),
+            w_down_f16=t.get("w_down_f16"), w_sh_down_f16=t.get("w_sh_down_f16"))
         self.ws_bytes = _lib.moe_workspace_size(self.ccfg)
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
         self.act_dtype = _TORCH_STORAGE[cfg.act]

@@ -49,9 +49,10 @@ def test_struct_layout_matches_c():
 #include <stddef.h>
 #include "moe.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(moe_config_t), offsetof(moe_config_t, routed_scaling_factor),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(moe_config_t), offsetof(moe_config_t, routed_scaling_factor),
          offsetof(moe_config_t, expert_dtype), offsetof(moe_config_t, expert_layout),
-         sizeof(moe_weights_t), offsetof(moe_weights_t, s_gate_up), offsetof(moe_weights_t, s_sh_down));
+         sizeof(moe_weights_t), offsetof(moe_weights_t, s_gate_up), offsetof(moe_weights_t, s_sh_down),
+         offsetof(moe_weights_t, w_sh_down_f16));
   return 0;
 }
 """
@@ -65,7 +66,7 @@ int main(void) {
     C, W = moe.moe_config_t, moe.moe_weights_t
     assert vals == [ctypes.sizeof(C), C.routed_scaling_factor.offset, C.expert_dtype.offset,
                     C.expert_layout.offset, ctypes.sizeof(W), W.s_gate_up.offset,
-                    W.s_sh_down.offset]
+                    W.s_sh_down.offset, W.w_sh_down_f16.offset]
 
 
 def test_status_strings_and_version():
@@ -163,6 +164,24 @@ def test_validation_rejects_before_launch():
     w8 = weights(s_gate_up=FAKE, s_down=FAKE, s_sh_gate_up=FAKE, s_sh_down=FAKE)
     for name in ("moe_layer_forward", "moe_layer_forward_fused"):
         assert call(name, by(c8s), by(w8), FAKE, FAKE, None, None, FAKE, n8, None) == moe.MOE_ERR_UNSUPPORTED
+    # optional fp16 down copies: bf16 experts only, shared copy required with
+    # S > 0, never the shared copy alone, 16-byte aligned
+    cb = cfg(act="bf16", expert="bf16")
+    both = dict(w_down_f16=FAKE, w_sh_down_f16=FAKE)
+    scales = dict(s_gate_up=FAKE, s_down=FAKE, s_sh_gate_up=FAKE, s_sh_down=FAKE)
+    for bad_w, bad_c in ((weights(**scales, **both), c8),
+                         (weights(**both), c), (weights(w_sh_down_f16=FAKE), cb),
+                         (weights(w_down_f16=FAKE), cb), (weights(w_down_f16=FAKE + 8, w_sh_down_f16=FAKE), cb),
+                         (weights(w_down_f16=FAKE, w_sh_down_f16=FAKE + 8), cb)):
+        nb = moe.moe_workspace_size(bad_c)
+        assert call("moe_layer_forward", by(bad_c), by(bad_w), FAKE, FAKE, None, None, FAKE, nb,
+                    None) == moe.MOE_ERR_INVALID_ARG
+    # fp16 conversion of bf16 weights: n a multiple of 8, aligned, no overlap
+    cv = "moe_convert_bf16_to_f16"
+    assert call(cv, FAKE, FAKE + 4096, 0, None) == moe.MOE_OK
+    for args in ((FAKE, FAKE + 4096, 12), (FAKE, FAKE + 4096, -8), (None, FAKE, 8), (FAKE, None, 8),
+                 (FAKE + 2, FAKE + 4096, 8), (FAKE, FAKE + 4096 + 8, 8), (FAKE, FAKE + 8, 16)):
+        assert call(cv, *args, None) == moe.MOE_ERR_INVALID_ARG, args
     # combine / dispatch / quantiser argument checks
     assert call("moe_combine", by(c), FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert call("moe_dispatch", by(c), FAKE, None, FAKE, FAKE, FAKE, FAKE, n, None) == moe.MOE_ERR_INVALID_ARG

@@ -153,3 +153,72 @@ def test_full_size_tiled_equals_row_major(cid):
         d = (a.float() - b.float()).abs()
         log(f"tiled full C{cid}: max |diff| {d.max().item():.3e}")
     assert same
+    if ek == "bf16":
+        # the benchmark's weights: tiled plus the fp16 copies of the down weights
+        f16 = {key: torch.empty(packed[key].shape, dtype=torch.float16, device="cuda")
+               for key in ("w_down", "w_sh_down")}
+        for key in f16:
+            moe.moe_convert_bf16_to_f16(packed[key], f16[key], packed[key].numel())
+        w16 = moe.make_weights(w_router=t["w_router"], router_bias=t["bias"],
+                               w_gate_up=packed["w_gate_up"], w_down=packed["w_down"],
+                               w_sh_gate_up=packed["w_sh_gate_up"], w_sh_down=packed["w_sh_down"],
+                               w_down_f16=f16["w_down"], w_sh_down_f16=f16["w_sh_down"])
+        c = lay.empty_out()
+        log(f"tiled full C{cid}: forward with fp16 down copies")
+        moe.moe_layer_forward(ct, w16, t["x"], c, workspace=lay.workspace)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.uint8), c.view(torch.uint8))
+
+
+def bf16_to_f16_rtz(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp16 bit patterns of the value rounded toward
+    zero, from the IEEE definition on the exact (fp64) value: exact on
+    fp16's normal range, the subnormal grid 2^-24 truncated below 2^-14,
+    +-65504 beyond the largest finite fp16, inf and NaN kept."""
+    with np.errstate(invalid="ignore"):  # NaN patterns
+        v = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    a = np.abs(v)
+    q = np.where(a < 2.0 ** -14, np.trunc(v * 2.0 ** 24) * 2.0 ** -24, v)
+    q = np.where(np.isfinite(v) & (a > 65504.0), np.sign(v) * 65504.0, q)
+    return q.astype(np.float16).view(np.uint16)
+
+
+def test_convert_bf16_to_f16_every_pattern():
+    """All 65536 bf16 patterns (normal, subnormal, zero, beyond fp16's range,
+    inf, NaN) against the rounding-toward-zero definition."""
+    bits = np.tile(np.arange(65536, dtype=np.uint16), 2)
+    src = torch.from_numpy(bits.view(np.int16)).cuda()
+    dst = torch.full_like(src, 0x5555)
+    moe.moe_convert_bf16_to_f16(src, dst, bits.size)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy().view(np.uint16)
+    ref = bf16_to_f16_rtz(bits)
+    nan = np.isnan(ref.view(np.float16))
+    assert np.isnan(got.view(np.float16)[nan]).all()
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+
+
+# the optional fp16 down copies: read only on the large-tile path, where
+# they replace the in-register conversion of the same bf16 values, so the
+# layer's output is the same bit for bit (and is ignored elsewhere)
+F16_CASES = {
+    "big_bf16": lambda: small(T=600, E=32, k=8, I=384),             # 150 rows/expert
+    "big_bf16_S2": lambda: small(T=640, H=768, E=16, S=2, k=4, I=512),  # 160
+    "big_bf16_S0": lambda: small(T=600, E=32, k=8, I=384, S=0),
+    "decode16": lambda: small(T=64, E=64, k=4),                     # ignored here
+}
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+@pytest.mark.parametrize("case", list(F16_CASES))
+def test_layer_down_f16_copy_equals_bf16(case, tiled):
+    cfg = F16_CASES[case]()
+    log(f"down f16 copy {case} tiled={tiled}: {cfg}")
+    inp = generate(cfg)
+    a = DeviceLayer(cfg, inp, tiled=tiled).forward()
+    lay = DeviceLayer(cfg, inp, tiled=tiled, down_f16=True)
+    b = lay.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"{case}: fp16 copy changed the output"
+    idx, w = layer_routing(moe, lay)
+    check_layer_output(cfg, inp, out_to_f64(b), idx, f"down f16 copy {case}", w_gpu=w)
