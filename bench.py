@@ -211,23 +211,33 @@ def time_calls(fn, iters, warmup):
     return e0.elapsed_time(e1) / iters
 
 
-def load_layer(cfg, tiled=True, keep_rows=False, keep_inputs=False):
+def load_layer(cfg, tiled=True, keep_rows=False, keep_inputs=False, down_f16=True):
     """Generate the seeded inputs of `cfg`, upload them and (tiled) pack the
-    expert weights once.  Returns (layer, row-major layer or None, host inputs
-    or None)."""
+    expert weights once; with bf16 experts and down_f16, also make the fp16
+    copies of the down weights (moe_convert_bf16_to_f16) once.  Returns
+    (layer, row-major layer or None, host inputs or None)."""
     import torch
+    import sparse_moe_expert_amd as moe
     from moe_inputs import generate
     from sparse_moe_expert_amd.device import DeviceLayer, pack_expert_weights
     t0 = time.perf_counter()
     inp = generate(cfg)
     log(f"bench: {cfg.name}: generated in {time.perf_counter() - t0:.1f}s; uploading")
+    f16 = down_f16 and cfg.expert == "bf16"
     if tiled and not keep_rows:
-        lay, rows = DeviceLayer(cfg, inp, tiled=True), None
+        lay, rows = DeviceLayer(cfg, inp, tiled=True, down_f16=f16), None
     else:
         rows = DeviceLayer(cfg, inp)
         lay = rows
         if tiled:
             packed = {key: pack_expert_weights(rows.t[key], cfg.expert) for key in EXPERT_KEYS}
+            if f16:
+                for key in ("w_down", "w_sh_down"):
+                    if packed[key].numel():
+                        packed[key + "_f16"] = torch.empty(packed[key].shape, dtype=torch.float16,
+                                                           device="cuda")
+                        moe.moe_convert_bf16_to_f16(packed[key], packed[key + "_f16"],
+                                                    packed[key].numel())
             lay = _view(rows, cfg, expert_t=packed, tiled=True)
     torch.cuda.synchronize()
     return lay, (rows if keep_rows else None), (inp if keep_inputs else None)
@@ -464,6 +474,9 @@ def main():
                     help="skip ceilings, grouped routing, block, copy and row-major lines")
     ap.add_argument("--weights", choices=("tiled", "rows"), default="tiled",
                     help="expert weight storage of the timed layer (default: packed tiles)")
+    ap.add_argument("--no-down-f16", action="store_true",
+                    help="no fp16 copies of the bf16 down weights (the large-tile down GEMM "
+                         "then converts its bf16 weight fragments in registers)")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run one plain device-to-device copy of this many GiB "
                          "(calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -485,8 +498,9 @@ def main():
     cfg = config(args.config)
     tiled = args.weights == "tiled"
     extras = not args.no_extras and args.config == 2
+    down_f16 = not args.no_down_f16 and cfg.expert == "bf16"
     lay, lay_rows, inp = load_layer(cfg, tiled=tiled, keep_rows=tiled and extras,
-                                    keep_inputs=not args.no_cpu_baseline)
+                                    keep_inputs=not args.no_cpu_baseline, down_f16=down_f16)
     held += [lay, lay_rows]
 
     log(f"bench: {args.warmup} warmup + {args.steps} timed steps")
@@ -509,7 +523,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "S": cfg.S,
                    "k": cfg.k, "I": cfg.I, "precision": dtype, "seed": 0,
-                   "expert_weights": "tiled16x64B" if tiled else "row_major"},
+                   "expert_weights": "tiled16x64B" if tiled else "row_major",
+                   "down_weights_fp16_copy": down_f16},
         "tflops": round(flops / (ms / 1e3) / 1e12, 2),
         "frac_of_peak_mfma_whole_step": round(flops / (ms / 1e3) / 1e12 / PEAK_TFLOPS[dtype], 4),
         "ms_per_step_instrumented": round(r["ms_inst"], 4),
@@ -523,7 +538,15 @@ def main():
     if lay_rows is not None:
         msr = time_layer(lay_rows, args.steps, args.warmup)["ms"]
         res["row_major_weights"] = {"ms_per_step": round(msr, 4),
-                                    "tokens_per_s": round(cfg.T / (msr / 1e3), 1)}
+                                    "tokens_per_s": round(cfg.T / (msr / 1e3), 1),
+                                    "down_weights_fp16_copy": False}
+    if extras and down_f16:
+        lay_nc = _view(lay, cfg, expert_t={"w_down_f16": None, "w_sh_down_f16": None})
+        rn = time_layer(lay_nc, args.steps, args.warmup)
+        res["without_down_f16_copy"] = {"ms_per_step": round(rn["ms"], 4),
+                                        "tokens_per_s": round(cfg.T / (rn["ms"] / 1e3), 1),
+                                        "stages_ms": stage_dict(rn)}
+        del lay_nc
     if extras:
         log("bench: grouped routing and block forward")
         res["grouped_routing"] = grouped_routing(lay, cfg)
@@ -610,7 +633,8 @@ def _view(lay, cfg1, inp1=None, expert_t=None, tiled=None):
         w_router=t["w_router"], router_bias=t["bias"], w_gate_up=t["w_gate_up"],
         w_down=t["w_down"], s_gate_up=t.get("s_gate_up"), s_down=t.get("s_down"),
         w_sh_gate_up=t["w_sh_gate_up"], w_sh_down=t["w_sh_down"],
-        s_sh_gate_up=t.get("s_sh_gate_up"), s_sh_down=t.get("s_sh_down"))
+        s_sh_gate_up=t.get("s_sh_gate_up"), s_sh_down=t.get("s_sh_down"),
+        w_down_f16=t.get("w_down_f16"), w_sh_down_f16=t.get("w_sh_down_f16"))
     v.ws_bytes = _lib.moe_workspace_size(v.ccfg)
     v.workspace = torch.empty(v.ws_bytes, dtype=torch.uint8, device="cuda")
     v.act_dtype = lay.act_dtype
