@@ -151,6 +151,29 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
   // (4 consecutive output columns of one token row per lane)
   constexpr bool TRN = (DUAL && F16) || YF16;
   static_assert(!YF16 || A16, "fp16 y comes from the projection of fp16 h");
+  // bf16 token rows (PAIR, all but the fp16-h projection): one load
+  // instruction covers 8 rows x 128 bytes, a pair of slices, so each
+  // 128-byte line of a row is read whole by one instruction (two slices of 64
+  // bytes read it half by half: gate/up 4.07 -> 3.78 ms at T=16384 in a
+  // timing copy).  Lane l reads row 8 h + (l / 4) % 8 of the wave's 16 (h
+  // alternates with the iteration) and chunk l % 4 of slice 2 pr + l / 32:
+  // 16 consecutive lanes write 4 rows of one slot, on distinct LDS banks.
+  // Four LDS slots: a pair's two slices are written while the two before
+  // them may still be read.
+  constexpr bool PAIR = !A16;
+  constexpr int UL = PAIR ? 4 : U;  // LDS slots of token slices
+  const char* ap[2] = {nullptr, nullptr};
+  int ap_dst[2] = {0, 0};
+  if constexpr (PAIR) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = wave * 16 + h * 8 + ((lane >> 2) & 7);
+      ap[h] = static_cast<const char*>(p.A) +
+              gemm_a_source_row(p, job.row_begin + job.m0 + min(r, job.rows_here - 1)) * rowb_a +
+              ((lane >> 5) * 4 + (lane & 3)) * 16;
+      ap_dst[h] = (lane >> 5) * A_SLOT + swz(r, lane & 3);
+    }
+  }
   uint32_t* mult_tab = reinterpret_cast<uint32_t*>(smem + U * A_SLOT);
   const int nb = p.exp_blocks;
   auto mult_of = [&](int kt) __attribute__((always_inline)) {
@@ -219,47 +242,94 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
     *reinterpret_cast<uint4*>(smem + slot * A_SLOT + a_dst) = v;
   };
 
+  // PAIR: half h of pair pr (slices 2 pr, 2 pr + 1; pairs past the end
+  // repeat the last one), and its store into the pair's two LDS slots (the
+  // first of them slot0 = 2 pr % 4)
+  auto load_pair = [&](uint4& dst, int pr, int h) __attribute__((always_inline)) {
+    dst = gload<uint4>(ap[h] + static_cast<long long>(kt0 + min(2 * pr, nk - 2)) * SLICE_B);
+  };
+  auto store_pair = [&](uint4 v, int slot0, int h) __attribute__((always_inline)) {
+    *reinterpret_cast<uint4*>(smem + slot0 * A_SLOT + ap_dst[h]) = v;
+  };
+
   // Slice kt: token rows loaded at iteration kt - 3 into a_stage[kt % 3],
   // written to LDS slot kt % 3 at iteration kt - 1, read at iteration kt;
-  // weights loaded at iteration kt - 2 into b_ring[kt % 3].  Loads past the
-  // last slice fetch the last slice again (never used), so every iteration
-  // runs the same instructions.
-  // prologue, in the order the iterations would have issued it: token rows
-  // of slices 0 .. U-1, weights of slices 0 .. U-2
-  load_a(a_stage[0], 0);
+  // weights loaded at iteration kt - 2 into b_ring[kt % 3].  PAIR: iteration
+  // kt loads half kt % 2 of pair (kt + 4) / 2 into a_stage[kt % 3] and stores
+  // the register loaded two iterations before (half kt % 2 of pair
+  // (kt + 2) / 2), so a pair is in LDS before the iteration of its first
+  // slice; slice kt is read from LDS slot kt % 4.  Loads past the last slice
+  // fetch the last slice again (never used), so every iteration runs the
+  // same instructions.
+  // prologue, in the order the iterations would have issued it
+  if constexpr (PAIR) {
+    uint4 t0, t1;
+    load_pair(t0, 0, 0);
+    load_pair(t1, 0, 1);
+    load_pair(a_stage[1], 1, 0);
+    load_b(b_ring[0], 0);
+    load_pair(a_stage[2], 1, 1);
+    load_b(b_ring[1], 1);
+    store_pair(t0, 0, 0);
+    store_pair(t1, 0, 1);
+  } else {
+    load_a(a_stage[0], 0);
 #pragma unroll
-  for (int j = 1; j < U; ++j) {
-    load_a(a_stage[j], j);
-    load_b(b_ring[j - 1], j - 1);
+    for (int j = 1; j < U; ++j) {
+      load_a(a_stage[j], j);
+      load_b(b_ring[j - 1], j - 1);
+    }
+    store_a(a_stage[0], 0, A16 ? mult_of(0) : 0u);
   }
-  store_a(a_stage[0], 0, A16 ? mult_of(0) : 0u);
 
   auto iter = [&](auto rc, int kt) __attribute__((always_inline)) {
-    constexpr int R = decltype(rc)::value;  // kt % U
+    constexpr int RR = decltype(rc)::value;  // kt % (PAIR ? 12 : U)
+    constexpr int R = RR % U;                // register rings
+    constexpr int RL = RR % UL;              // LDS slot of slice kt
     const uint32_t mb = A16 ? mult_of(kt + 1) : 0u;  // completes with the barrier's wait
     slice_barrier();                        // slice kt is in LDS for every wave
-    store_a(a_stage[(R + 1) % U], (R + 1) % U, mb);
-    load_a(a_stage[R], kt + U);
+    if constexpr (PAIR) {
+      store_pair(a_stage[(R + 1) % U], (((RR + 2) >> 1) * 2) % 4, RR & 1);
+      load_pair(a_stage[R], (kt + 4) >> 1, RR & 1);
+    } else {
+      store_a(a_stage[(R + 1) % U], (R + 1) % U, mb);
+      load_a(a_stage[R], kt + U);
+    }
     load_b(b_ring[(R + U - 1) % U], kt + U - 1);
     if constexpr (MS > 0 && !A16) {
-      const char* As = smem + R * A_SLOT;
+      const char* As = smem + RL * A_SLOT;
+      // fragments in two halves: the second half's LDS reads run under the
+      // first half's MFMAs, and the two halves share registers
+      constexpr int MH = MS / 2;
       bf16x8 af[8];
 #pragma unroll
-      for (int m = 0; m < MS; ++m)
+      for (int m = 0; m < MH; ++m)
         af[m] = *reinterpret_cast<const bf16x8*>(As + swz(m * 16 + (lane & 15), lane >> 4));
 #pragma unroll
-      for (int m = 0; m < MS; ++m)
+      for (int m = 0; m < MH; ++m)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           acc[m][t] = TRN ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(b_ring[R][t], af[m], acc[m][t], 0, 0, 0)
                           : __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], b_ring[R][t], acc[m][t], 0, 0, 0);
-      // instruction order: all fragment reads, the LDS write of the next
-      // slice, then the MFMAs with the five global loads spread among them
-      __builtin_amdgcn_sched_group_barrier(0x100, MS, 0);  // DS read
+#pragma unroll
+      for (int m = MH; m < MS; ++m)
+        af[m] = *reinterpret_cast<const bf16x8*>(As + swz(m * 16 + (lane & 15), lane >> 4));
+#pragma unroll
+      for (int m = MH; m < MS; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[m][t] = TRN ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(b_ring[R][t], af[m], acc[m][t], 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], b_ring[R][t], acc[m][t], 0, 0, 0);
+      // instruction order: the first half's fragment reads, the LDS write of
+      // a later slice, the first half's MFMAs with the second half's reads
+      // after the first four, then the second half's MFMAs; the five global
+      // loads spread among the MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, MH, 0);  // DS read
       __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
 #pragma unroll
       for (int i = 0; i < MS * NT; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if (i == MH * NT - 1) __builtin_amdgcn_sched_group_barrier(0x100, MS - MH, 0);  // DS read
         if (i % 4 == 3 && i / 4 < 1 + NT) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
       }
     }
@@ -298,13 +368,14 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
     }
   };
   int kt = 0;
-  auto run = [&](auto... rs) __attribute__((always_inline)) {  // U iterations, R = 0 .. U-1
-    for (; kt + U <= nk; kt += U) (iter(rs, kt + decltype(rs)::value), ...);
+  constexpr int PER = PAIR ? 12 : U;  // the rings' common period
+  auto run = [&](auto... rs) __attribute__((always_inline)) {  // PER iterations, RR = 0 .. PER-1
+    for (; kt + PER <= nk; kt += PER) (iter(rs, kt + decltype(rs)::value), ...);
     ((kt + decltype(rs)::value < nk ? iter(rs, kt + decltype(rs)::value) : void()), ...);
   };
   [&]<int... Rs>(std::integer_sequence<int, Rs...>) __attribute__((always_inline)) {
     run(std::integral_constant<int, Rs>{}...);
-  }(std::make_integer_sequence<int, U>{});
+  }(std::make_integer_sequence<int, PER>{});
 
   // ------------------------------------------------------------ epilogue
   // 16x16 accumulator layout: lane l, element i -> row 4 (l / 16) + i (token),
@@ -592,6 +663,9 @@ hipError_t launch_prefill(const GemmLaunch& g, hipStream_t st) {
     return hipErrorInvalidValue;
   if (g.c_exp && g.c_exp_blocks != (g.N + kHBlock - 1) / kHBlock) return hipErrorInvalidValue;
   if (yf16 && !f16) return hipErrorInvalidValue;  // fp16 y only from fp16 h
+  // bf16 token rows go in pairs of slices: an even slice count per block
+  // (K a multiple of 64 elements per split; H and I are multiples of 128)
+  if (!(f16 && !DUAL) && (g.K / KE / splits) % 2 != 0) return hipErrorInvalidValue;
   const bool w16 = !DUAL && g.w16;
   if ((g.w16 && DUAL) || (w16 && !f16)) return hipErrorInvalidValue;  // fp16 weights meet fp16 h only
   if constexpr (!DUAL) {
