@@ -179,19 +179,41 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
   auto mult_of = [&](int kt) __attribute__((always_inline)) {
     return mult_tab[ar * nb + (kt0 + min(kt, nk - 1)) * KE / kHBlock];
   };
+  // A16: the staging row's block exponents.  Up to kExpRegs blocks (K up to
+  // 2048) they are loaded into registers before the first slices' loads are
+  // issued and used after them, so the two memory round trips overlap (the
+  // loads complete in order: waiting for the exponents leaves the slices in
+  // flight); more blocks are read after the first slices' loads.
+  constexpr int kExpRegs = 8;
+  const int32_t* ex = nullptr;
+  int exv[kExpRegs];
   if constexpr (A16) {
-    const int32_t* ex = p.a_exp + static_cast<long long>(job.row_begin + job.m0 +
-                                                         min(ar, job.rows_here - 1)) * nb;
-    int e_row = ex[0];
-    for (int b = 1; b < nb; ++b) e_row = max(e_row, ex[b]);
-    for (int b = ac; b < nb; b += 4)
-      mult_tab[ar * nb + b] = __builtin_bit_cast(uint32_t, pow2_neg_f16x2(e_row - ex[b]));
+    ex = p.a_exp + static_cast<long long>(job.row_begin + job.m0 + min(ar, job.rows_here - 1)) * nb;
+    if (nb <= kExpRegs) {
+#pragma unroll
+      for (int b = 0; b < kExpRegs; ++b) exv[b] = b < nb ? ex[b] : INT_MIN;
+    }
+  }
+  auto block_shifts = [&]() __attribute__((always_inline)) {
+    int e_row = INT_MIN;
+    if (nb <= kExpRegs) {
+#pragma unroll
+      for (int b = 0; b < kExpRegs; ++b) e_row = max(e_row, exv[b]);
+#pragma unroll
+      for (int b = 0; b < kExpRegs; ++b)
+        if (b < nb && (b & 3) == ac)
+          mult_tab[ar * nb + b] = __builtin_bit_cast(uint32_t, pow2_neg_f16x2(e_row - exv[b]));
+    } else {
+      for (int b = 0; b < nb; ++b) e_row = max(e_row, ex[b]);
+      for (int b = ac; b < nb; b += 4)
+        mult_tab[ar * nb + b] = __builtin_bit_cast(uint32_t, pow2_neg_f16x2(e_row - ex[b]));
+    }
     if (ac == 0) erow[ar] = e_row;
     // the shifts of a row are read by the other lanes of this wave
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
+  };
   // weight tiles of this wave: lane l reads row l % 16 of the tile, bytes
   // [16 (l / 16), +16) of the slice.  Rows past N (a partial last tile, or
   // the router's N = E below 16) read row N - 1 instead: in bounds, and the
@@ -279,6 +301,7 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
       load_a(a_stage[j], j);
       load_b(b_ring[j - 1], j - 1);
     }
+    if constexpr (A16) block_shifts();
     store_a(a_stage[0], 0, A16 ? mult_of(0) : 0u);
   }
 
