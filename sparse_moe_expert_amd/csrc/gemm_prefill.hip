@@ -319,30 +319,37 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
       load_a(a_stage[R], kt + U);
     }
     load_b(b_ring[(R + U - 1) % U], kt + U - 1);
-    if constexpr (MS > 0 && !A16) {
+    if constexpr (MS > 0 && (!A16 || W16)) {
       const char* As = smem + RL * A_SLOT;
       // fragments in two halves: the second half's LDS reads run under the
-      // first half's MFMAs, and the two halves share registers
+      // first half's MFMAs, and the two halves share registers (fp16 h with
+      // fp16 weights: the same schedule with fp16 MFMAs)
       constexpr int MH = MS / 2;
       bf16x8 af[8];
+      auto mma = [&](int m, int t) __attribute__((always_inline)) {
+        if constexpr (A16) {
+          const half8 a = __builtin_bit_cast(half8, af[m]), w = __builtin_bit_cast(half8, b_ring[R][t]);
+          acc[m][t] = TRN ? __builtin_amdgcn_mfma_f32_16x16x32_f16(w, a, acc[m][t], 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_16x16x32_f16(a, w, acc[m][t], 0, 0, 0);
+        } else {
+          acc[m][t] = TRN ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(b_ring[R][t], af[m], acc[m][t], 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], b_ring[R][t], acc[m][t], 0, 0, 0);
+        }
+      };
 #pragma unroll
       for (int m = 0; m < MH; ++m)
         af[m] = *reinterpret_cast<const bf16x8*>(As + swz(m * 16 + (lane & 15), lane >> 4));
 #pragma unroll
       for (int m = 0; m < MH; ++m)
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          acc[m][t] = TRN ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(b_ring[R][t], af[m], acc[m][t], 0, 0, 0)
-                          : __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], b_ring[R][t], acc[m][t], 0, 0, 0);
+        for (int t = 0; t < NT; ++t) mma(m, t);
 #pragma unroll
       for (int m = MH; m < MS; ++m)
         af[m] = *reinterpret_cast<const bf16x8*>(As + swz(m * 16 + (lane & 15), lane >> 4));
 #pragma unroll
       for (int m = MH; m < MS; ++m)
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          acc[m][t] = TRN ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(b_ring[R][t], af[m], acc[m][t], 0, 0, 0)
-                          : __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], b_ring[R][t], acc[m][t], 0, 0, 0);
+        for (int t = 0; t < NT; ++t) mma(m, t);
       // instruction order: the first half's fragment reads, the LDS write of
       // a later slice, the first half's MFMAs with the second half's reads
       // after the first four, then the second half's MFMAs; the five global
@@ -356,7 +363,7 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
         if (i % 4 == 3 && i / 4 < 1 + NT) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
       }
     }
-    if constexpr (MS > 0 && A16) {
+    if constexpr (MS > 0 && A16 && !W16) {
       // fp16 A fragments; weight tile t converted to fp16 just before its
       // MS MFMAs (weight tile major, so each conversion overlaps the MFMAs
       // of the tile before)
@@ -367,7 +374,7 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
         af[m] = *reinterpret_cast<const half8*>(As + swz(m * 16 + (lane & 15), lane >> 4));
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const half8 bf = W16 ? __builtin_bit_cast(half8, b_ring[R][t]) : bf16x8_to_f16(b_ring[R][t]);
+        const half8 bf = bf16x8_to_f16(b_ring[R][t]);
 #pragma unroll
         for (int m = 0; m < MS; ++m)
           acc[m][t] = TRN ? __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, af[m], acc[m][t], 0, 0, 0)
@@ -380,7 +387,7 @@ __device__ __forceinline__ void tile_body(GemmLaunch& p, const TileJob& job, cha
       __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if constexpr (!W16) __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
