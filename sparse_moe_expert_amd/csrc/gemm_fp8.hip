@@ -47,7 +47,6 @@ constexpr int S = D + 1;                    // ring slots (weights and tokens)
 constexpr int A_SLOT = BM * STEP;           // 24 KB of token rows per step
 constexpr int A_DMA = A_SLOT / 16 / THREADS;  // 16-byte DMA chunks per thread per step: 3
 constexpr int W_LOADS = 4;                  // 16-byte weight loads per thread per step
-constexpr int OPS = A_DMA + W_LOADS;        // vector memory ops per thread per step
 constexpr int MAX_KB = 64;                  // K <= 8192
 constexpr int kXcdChunk = 32;               // tiles per XCD chunk: one block per CU, 32 CUs per XCD
 constexpr int SA_OFF = S * A_SLOT;          // token scales [kb][row] fp32
@@ -89,9 +88,14 @@ __device__ __forceinline__ i32x4_t gload16(const char* p) {
 }
 
 // MT: 16-row token tiles computed (4, 8 or 12; the ragged rows past the
-// tile's last row in the last of them are computed and never stored).
+// tile's last row in the last of them are computed and never stored).  Only
+// those MT * 16 rows are brought in: AD = MT / 4 DMA chunks per thread and
+// step (a tile of 65-128 rows moves 16 KB of token rows per step, not 24).
 template <bool DUAL, int MT>
 __device__ __forceinline__ void tile_body(const GemmLaunch& p, const TileJob& job, char* smem) {
+  static_assert(MT % 4 == 0 && MT / 4 <= A_DMA, "64-row groups of the 192-row tile");
+  constexpr int AD = MT / 4;          // 16-byte DMA chunks per thread per step
+  constexpr int OPS = AD + W_LOADS;   // vector memory ops per thread per step
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -104,9 +108,9 @@ __device__ __forceinline__ void tile_body(const GemmLaunch& p, const TileJob& jo
   // (j * WAVES + wave) * 8 + lane / 8 at physical chunk lane % 8 (rows past
   // the tile's last row repeat it: every thread issues the same number of
   // loads per step, which the step's vmcnt wait counts on)
-  const char* a_src[A_DMA];
+  const char* a_src[AD];
 #pragma unroll
-  for (int j = 0; j < A_DMA; ++j) {
+  for (int j = 0; j < AD; ++j) {
     const int r = (j * WAVES + wave) * 8 + (lane >> 3);
     const int lchunk = (lane & 7) ^ swz_key(r);
     const int src = gemm_a_source_row(p, job.row_begin + job.m0 + min(r, job.rows_here - 1));
@@ -139,10 +143,11 @@ __device__ __forceinline__ void tile_body(const GemmLaunch& p, const TileJob& jo
     sb_val = job.WS[static_cast<long long>(rb) * kblocks + kb];
     sb_slot = q * MAX_KB + kb;
   }
-  // token scales sa_tab[kb * BM + r] by 4-byte DMA, 64 rows of one K block per
-  // instruction; every wave issues the same number (the last repeated)
+  // token scales sa_tab[kb * BM + r] of the tile's MT * 16 rows by 4-byte
+  // DMA, 64 rows of one K block per instruction; every wave issues the same
+  // number (the last repeated)
   {
-    const int per_kb = BM / 64;
+    const int per_kb = AD;
     const int total = per_kb * nk;
     const int n_iss = (total + WAVES - 1) / WAVES;
     for (int i = 0; i < n_iss; ++i) {
@@ -169,7 +174,7 @@ __device__ __forceinline__ void tile_body(const GemmLaunch& p, const TileJob& jo
     }
     char* base = smem + R * A_SLOT;
 #pragma unroll
-    for (int j = 0; j < A_DMA; ++j)
+    for (int j = 0; j < AD; ++j)
       __builtin_amdgcn_global_load_lds(a_src[j] + ks * STEP,
                                        (lds_ptr_t)(base + (j * WAVES + wave) * 1024), 16, 0, 0);
   };
