@@ -9,6 +9,22 @@ namespace moe {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// 16-byte weight load.  STREAM (expert weights): each touched expert's
+// matrix is read exactly once per launch, so the load is marked
+// non-temporal and the weight stream does not displace the cached token rows
+// (measured at T=256: gate/up 1.360 -> 1.258 ms, down 0.745 -> 0.670 ms).  The
+// router weight is read by every token tile and stays a cached load.
+typedef int w16_vec_t __attribute__((ext_vector_type(4)));
+template <bool STREAM>
+__device__ __forceinline__ uint4 load_weights16(const char* ptr) {
+  if constexpr (STREAM)
+    return __builtin_bit_cast(
+        uint4, __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) w16_vec_t*>(
+                   reinterpret_cast<uintptr_t>(ptr))));
+  else
+    return *reinterpret_cast<const uint4*>(ptr);
+}
+
 template <int MT, int NT, int NA>
 struct Regs {
   uint4 a[NA][MT][4];  // NA = 2: A and its bf16 residue A_lo
@@ -17,8 +33,9 @@ struct Regs {
 
 // One 4-wave tile (block index b, see find_tile_at) of the decode GEMM.
 // LO (projection only): A is a two-term bf16 split, A + A_lo (p.A_lo), and
-// both terms multiply the same weight fragments.
-template <int MT, bool DUAL, int NT, bool LO = false>
+// both terms multiply the same weight fragments.  STREAM: the weights are
+// expert weights, read once per launch (non-temporal loads).
+template <int MT, bool DUAL, int NT, bool LO = false, bool STREAM = true>
 __device__ __forceinline__ void decode_tile(const GemmLaunch& p, int b) {
   static_assert(!(DUAL && LO), "the two-term A is the down projection's input");
   constexpr int NA = LO ? 2 : 1;
@@ -82,7 +99,7 @@ __device__ __forceinline__ void decode_tile(const GemmLaunch& p, int b) {
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        R.b[t][s] = *reinterpret_cast<const uint4*>(bptr[t] + off_b + s * s_stride_b);
+        R.b[t][s] = load_weights16<STREAM>(bptr[t] + off_b + s * s_stride_b);
 #pragma unroll
     for (int q = 0; q < NA; ++q)
 #pragma unroll
