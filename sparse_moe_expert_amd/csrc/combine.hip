@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   __shared__ float ws[kMaxTopK];
   __shared__ long long rs[kMaxTopK];
   // block (t, part): a 1/gridDim.y share of token t's columns
-  const int per = (H / static_cast<int>(gridDim.y) + 3) & ~3;
+  const int per = (H / static_cast<int>(gridDim.y) + 7) & ~7;
   const int c0 = static_cast<int>(blockIdx.y) * per;
   const int c1 = min(H, c0 + per);
   combine_token<OK, YF16>(y, ysh, w, inv, residual, out, T, H, k, S, blockIdx.x, ws, rs, c0, c1,

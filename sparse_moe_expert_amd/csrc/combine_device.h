@@ -9,7 +9,7 @@
 
 namespace moe {
 
-// Columns [c0, c1) of token t (multiples of 4), by one workgroup (every
+// Columns [c0, c1) of token t (multiples of 8), by one workgroup (every
 // thread of it calls this; it holds one workgroup barrier).  ws / rs:
 // kMaxTopK entries of LDS each.  Each output element is summed by one thread
 // in the fixed order (residual, shared experts, slots j ascending), so the
@@ -48,6 +48,49 @@ __device__ __forceinline__ void combine_token(const void* __restrict__ y_,
     rs[threadIdx.x] = inv[static_cast<long long>(t) * k + threadIdx.x];
   }
   __syncthreads();
+  if constexpr (YF16) {
+    // scaled fp16 y (bf16 layers): 8 columns per thread, so each row is read
+    // with one 16-byte load (8 codes inside one exponent block; c0 and c1
+    // are multiples of 8).  Same terms in the same order as below.
+    static_assert(!YF16 || OK == K_BF16, "scaled fp16 y belongs to bf16 layers");
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    auto add8 = [&](float* acc, const void* base, long long row, long long drow, int c, float wj,
+                    bool fma) __attribute__((always_inline)) {
+      const h8 u = __builtin_nontemporal_load(
+          reinterpret_cast<const h8*>(static_cast<const uint16_t*>(base) + drow * H + c));
+      const int e = yexp[row * yeb + c / kHBlock];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = ldexpf(static_cast<float>(u[i]), e);
+        acc[i] = fma ? fmaf(wj, v, acc[i]) : acc[i] + v;
+      }
+    };
+    for (int c = c0 + threadIdx.x * 8; c < c1; c += blockDim.x * 8) {
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (residual) {
+        const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(residual) +
+                                                        static_cast<long long>(t) * H + c);
+        const uint32_t r4[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = bf16_to_f32(static_cast<uint16_t>(r4[i] & 0xFFFF));
+          acc[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(r4[i] >> 16));
+        }
+      }
+      for (int s = 0; s < S; ++s) {
+        const long long srow = static_cast<long long>(s) * T + t;
+        add8(acc, ysh_, R + srow, srow, c, 1.f, false);
+      }
+      for (int j = 0; j < k; ++j) add8(acc, y_, rs[j], rs[j], c, ws[j], true);
+      uint4 o;
+      o.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
+      o.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
+      o.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
+      o.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + static_cast<long long>(t) * H + c) = o;
+    }
+    return;
+  }
   for (int c = c0 + threadIdx.x * 4; c < c1; c += blockDim.x * 4) {
     float4 acc = float4{0.f, 0.f, 0.f, 0.f};
     if (residual) {
