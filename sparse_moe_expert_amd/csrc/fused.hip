@@ -31,14 +31,16 @@
 // fence after the wait: an acquire per poll invalidates the caches under the
 // blocks still working (measured 2.71 against 2.47 ms at T=256).
 //
-// Measured at T=256 (dots3 decode shape, tiled weights), block 0's time
-// from barrier to barrier: A 66, B 60, C 44, D 1432, E 819, F 34 us, 2.45 ms
-// in all, against 2.15 ms for the separate launches (route 27, dispatch 12,
-// gate/up 1362, down 751, combine 13 us).  The phases around the GEMMs take
-// 204 us here against 52 us as kernels: each of the five barriers, 512
-// blocks arriving on one counter, costs tens of microseconds, more than the
-// launch gaps they replace; the GEMM phases run 5% and 9% slower than the
-// separate kernels.
+// Measured at T=256 (dots3 decode shape, tiled weights, expert weights read
+// with cached loads at the time), block 0's time from barrier to barrier:
+// A 66, B 60, C 44, D 1432, E 819, F 34 us, 2.45 ms in all, against 2.15 ms
+// for the separate launches (route 27, dispatch 12, gate/up 1362, down 751,
+// combine 13 us).  The phases around the GEMMs take 204 us here against
+// 52 us as kernels: each of the five barriers, 512 blocks arriving on one
+// counter, costs tens of microseconds, more than the launch gaps they
+// replace; the GEMM phases run 5% and 9% slower than the separate kernels.
+// With the non-temporal expert weight loads both forms got faster, and the
+// gap stayed: 2.27 ms in one launch against 1.96 ms separately.
 #include <algorithm>
 
 #include "combine_device.h"
