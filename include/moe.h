@@ -411,7 +411,8 @@ moe_status_t moe_layer_forward_timed(const moe_config_t* cfg, const moe_weights_
                                      void* const* events);
 
 /* Measurement utility, no step of the layer: reads `bytes` (a multiple of
- * 16) of device memory at src (16-byte aligned) as one streaming pass with
+ * 16) of device memory at src (16-byte aligned) as one streaming pass
+ * (non-temporal loads, as the decode GEMMs read their weights) with
  * `blocks` workgroups of 256 threads (1..65536), and writes one folded word
  * per block to sink[0, blocks) so the reads cannot be elided.  Its rate is
  * the read ceiling the weight-streaming (decode) GEMMs are compared with.

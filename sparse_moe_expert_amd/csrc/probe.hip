@@ -1,8 +1,10 @@
 // Streaming-read kernel: the measured HBM read ceiling the benchmark sets the
 // weight-streaming GEMMs against (the vendor's 8 TB/s is a peak, not what a
 // read stream reaches).  Every lane reads 16-byte chunks over a grid-stride
-// loop, four loads in flight, and folds them into one word per block so the
-// loads cannot be dropped.  No arithmetic of the layer.
+// loop, four loads in flight, with the non-temporal hint the decode GEMMs
+// give their weight stream (every byte is read once), and folds them into
+// one word per block so the loads cannot be dropped.  No arithmetic of the
+// layer.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -11,6 +13,13 @@ namespace {
 
 constexpr int kThreads = 256;
 
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                       reinterpret_cast<const __attribute__((address_space(1))) i32x4_t*>(
+                                           reinterpret_cast<uintptr_t>(p))));
+}
+
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __restrict__ src,
                                                                long long chunks,
                                                                uint32_t* __restrict__ sink) {
@@ -18,12 +27,13 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __re
   long long q = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
   uint32_t acc = 0;
   for (; q + 3 * stride < chunks; q += 4 * stride) {
-    const uint4 a = src[q], b = src[q + stride], c = src[q + 2 * stride], d = src[q + 3 * stride];
+    const uint4 a = stream_load(src + q), b = stream_load(src + q + stride),
+                c = stream_load(src + q + 2 * stride), d = stream_load(src + q + 3 * stride);
     acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^
            d.z ^ d.w;
   }
   for (; q < chunks; q += stride) {
-    const uint4 a = src[q];
+    const uint4 a = stream_load(src + q);
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
 #pragma unroll

@@ -159,6 +159,9 @@ BLOCK_CASES = {
     "bf16_small": lambda: small(T=150, H=512, E=16, S=1, k=4, I=256),
     "bf16_grouped": lambda: small(T=150, H=512, E=32, S=2, k=4, I=256, n_group=4, topk_group=2),
     "fp8_small": lambda: small(T=200, H=512, E=16, S=1, k=4, I=1536, expert="fp8"),
+    # large-tile path: the residual joins the scaled fp16 y in a combine split
+    # over 2 blocks per token
+    "bf16_large_tile_split2": lambda: small(T=512, H=2048, E=8, S=1, k=2, I=256),
 }
 
 
@@ -173,8 +176,32 @@ def _block(cfg, inp, lay, g_st):
     return out, counts, ties
 
 
+def _normed_rows(cfg, inp, lay, g_st, g, where):
+    """The block's normalised rows (moe_rmsnorm: the kernel the block runs),
+    checked against the oracle's RMSNorm: bf16 rows equal the oracle's
+    rounding of the exact value or lie one bf16 step from it where the two
+    straddle a rounding boundary (as in test_rmsnorm_matches_oracle); fp32
+    rows within 2e-6 relative.  Returns them in storage format."""
+    xn = torch.empty_like(lay.t["x"])
+    moe.moe_rmsnorm(lay.ccfg, lay.t["x"], to_device(g_st, cfg.act), cfg.rms_norm_eps, xn)
+    torch.cuda.synchronize()
+    _, xn_ref = oracle.block_inputs(cfg, inp, g)
+    ref = oracle.widen(xn_ref, cfg.act)
+    got = out_to_f64(xn)
+    if cfg.act == "bf16":
+        step = np.abs(oracle.decode_bf16(xn_ref + 1) - ref)
+        assert np.all(np.abs(got - ref) <= step * 1.0001), f"{where}: RMSNorm rows"
+        return xn.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.all(np.abs(got - ref) <= 2e-6 * np.maximum(np.abs(ref), 1e-30)), f"{where}: RMSNorm rows"
+    return xn.cpu().numpy().astype(np.float32)
+
+
 @pytest.mark.parametrize("case", list(BLOCK_CASES))
 def test_block_forward_small(case):
+    """The normalised rows are checked against the oracle's RMSNorm; routing
+    and every output token against the oracle's layer on the block's own
+    normalised rows (a row one bf16 step off at a rounding boundary moves its
+    router scores by ~1e-5), with the block's choice of experts."""
     cfg = BLOCK_CASES[case]()
     log(f"block {case}: {cfg}")
     inp = generate(cfg)
@@ -182,13 +209,17 @@ def test_block_forward_small(case):
     g_st, g = gamma_for(cfg)
     out, counts, _ = _block(cfg, inp, lay, g_st)
     idx, w = layer_routing(moe, lay)
-    ref0, res0 = oracle.block_forward(cfg, inp, g)
+    inp_n = dict(inp)
+    inp_n["x"] = _normed_rows(cfg, inp, lay, g_st, g, f"block {case}")
+    tokens = np.arange(cfg.T)
+    res0 = oracle.layer_forward(cfg, inp_n, tokens)
     check_routing(cfg, res0.routing, idx, w, f"block {case} routing")
     # every token, against the oracle evaluated with the block's own choice
-    ref, res = oracle.block_forward(cfg, inp, g, idx=idx)
+    res = oracle.layer_forward(cfg, inp_n, tokens, idx=idx)
+    h = oracle.widen(inp["x"], cfg.act)
+    ref = h + res.out
     assert_close(cfg, out_to_f64(out), ref, f"block {case}")
     # the MoE part alone, against the layer output of the oracle
-    h = oracle.widen(inp["x"], cfg.act)
     moe_part = out_to_f64(out) - h
     rnd = np.abs(ref) * (2.0 ** -8 if cfg.act == "bf16" else 2.0 ** -23)
     err = np.abs(moe_part - res.out) - rnd

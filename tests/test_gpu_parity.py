@@ -275,6 +275,10 @@ LAYER_CASES = {
     "bf16_T4096_E1_dense": lambda: small(T=4096, H=512, E=1, S=0, k=1, I=256),
     "bf16_T4096_E8": lambda: small(T=4096, H=256, E=8, S=1, k=2, I=128),
     "bf16_T4096_E100": lambda: small(T=4096, H=512, E=100, S=1, k=4, I=128),
+    # large-tile path (scaled fp16 h and y) with the combine splitting each
+    # token's columns over 2 and 4 blocks (T < 1024, H >= 2048)
+    "bf16_large_tile_combine_split2": lambda: small(T=512, H=2048, E=8, S=1, k=2, I=256),
+    "bf16_large_tile_combine_split4": lambda: small(T=256, H=4096, E=4, S=1, k=2, I=256),
 }
 
 
